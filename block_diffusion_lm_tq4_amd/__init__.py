@@ -1,1 +1,9 @@
-"""TQ4_1S dequantize-and-multiply library for MI355X (gfx950)."""
+"""TQ4_1S ("Config-I") dequantize-and-multiply library for AMD MI355X (gfx950).
+
+The kernels live in ``libtq4.so`` (C ABI in ``include/tq4.h``), built in-tree
+by ``block_diffusion_lm_tq4_amd.build``.  ``ops`` is the torch-facing binding;
+``inputs`` holds the seeded synthetic workloads.
+"""
+
+from .ops import (act_rht, codebook, linear, linear_workspace_size, moe_grouped,  # noqa: F401
+                  moe_route, moe_workspace_size, pack, packed_size)

@@ -1,0 +1,220 @@
+// C ABI of the TQ4_1S library: argument validation, workspace layout and
+// dispatch.  Every argument check happens before any HIP call, so invalid
+// calls return without touching the GPU (and can be tested without one).
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/tq4.h"
+#include "tq4_internal.h"
+
+namespace {
+
+using tq4::DensePlan;
+using tq4::MoEPlan;
+using tq4::MoETile;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int device_status(hipError_t e) { return e == hipSuccess ? TQ4_OK : TQ4_E_DEVICE; }
+
+// ---- tq4_linear workspace: [xt fp16 m*k][partials][counters] -------------
+struct LinearLayout {
+  size_t xt, partial, counters, total;
+};
+
+LinearLayout linear_layout(int64_t m, int64_t k, int64_t n, const DensePlan &p) {
+  LinearLayout l{};
+  l.xt = 0;
+  l.partial = align_up(static_cast<size_t>(m) * k * 2);
+  l.counters = l.partial + align_up(p.partial_bytes);
+  l.total = l.counters + align_up(p.counter_bytes);
+  return l;
+}
+
+// ---- tq4_moe_grouped workspace ------------------------------------------
+struct MoELayout {
+  size_t counts, offsets, perm, inv, tiles, meta, xt, h, ht, o, total;
+};
+
+MoELayout moe_layout(int64_t t, int32_t topk, int32_t e, int64_t n1, int64_t k,
+                     const MoEPlan &p) {
+  const size_t pairs = static_cast<size_t>(t) * topk;
+  MoELayout l{};
+  size_t off = 0;
+  l.counts = off;  off += align_up(sizeof(int32_t) * e);
+  l.offsets = off; off += align_up(sizeof(int32_t) * (e + 1));
+  l.perm = off;    off += align_up(sizeof(int32_t) * pairs);
+  l.inv = off;     off += align_up(sizeof(int32_t) * pairs);
+  l.tiles = off;   off += align_up(sizeof(MoETile) * p.max_tiles);
+  l.meta = off;    off += kAlign;  // [0] tile count, [1] bad-id count
+  l.xt = off;      off += align_up(static_cast<size_t>(t) * k * 2);
+  l.h = off;       off += align_up(pairs * n1 * 4);
+  l.ht = off;      off += align_up(pairs * n1 * 2);
+  l.o = off;       off += align_up(pairs * k * 4);
+  l.total = off;
+  return l;
+}
+
+bool moe_shape_ok(int64_t t, int32_t topk, int32_t e, int64_t n1, int64_t k) {
+  if (t < 0 || topk < 1 || e < 1 || e > 512 || topk > e) return false;
+  if (n1 <= 0 || k <= 0 || n1 % 32 != 0 || k % 32 != 0) return false;
+  const MoEPlan p = tq4::plan_moe(t * topk, e);
+  if (p.max_tiles > 65535) return false;
+  if (t * topk > INT32_MAX) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tq4_status_string(int status) {
+  switch (status) {
+    case TQ4_OK: return "ok";
+    case TQ4_E_NULL: return "required pointer is NULL";
+    case TQ4_E_SHAPE: return "size out of range";
+    case TQ4_E_ALIGN: return "pointer misaligned";
+    case TQ4_E_WORKSPACE: return "workspace missing or too small";
+    case TQ4_E_DEVICE: return "HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int tq4_version(void) { return 100; }
+
+int tq4_codebook(float *out) {
+  if (out == nullptr) return TQ4_E_NULL;
+  memcpy(out, tq4::codebook().c, sizeof(float) * 16);
+  return TQ4_OK;
+}
+
+size_t tq4_packed_size(int64_t n, int64_t k) {
+  if (n < 0 || k < 0 || k % 32 != 0) return 0;
+  return static_cast<size_t>(n) * static_cast<size_t>(k / 32) * 20;
+}
+
+int tq4_pack(const float *w, int64_t n, int64_t k, uint32_t sign_bits, uint8_t *packed,
+             int32_t *nonfinite_count, void *stream) {
+  if (n < 0 || k < 0 || k % 32 != 0) return TQ4_E_SHAPE;
+  if (n == 0 || k == 0) return TQ4_OK;
+  if (w == nullptr || packed == nullptr) return TQ4_E_NULL;
+  if (!aligned(w, 16) || !aligned(packed, 4) ||
+      (nonfinite_count != nullptr && !aligned(nonfinite_count, 4)))
+    return TQ4_E_ALIGN;
+  return device_status(
+      tq4::launch_pack(w, n * (k / 32), sign_bits, packed, nonfinite_count, as_stream(stream)));
+}
+
+int tq4_act_rht(const uint16_t *x_bf16, int64_t m, int64_t k, uint32_t sign_bits,
+                uint16_t *xt_f16, void *stream) {
+  if (m < 0 || k < 0 || k % 32 != 0) return TQ4_E_SHAPE;
+  if (m == 0 || k == 0) return TQ4_OK;
+  if (x_bf16 == nullptr || xt_f16 == nullptr) return TQ4_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(xt_f16, 16)) return TQ4_E_ALIGN;
+  return device_status(tq4::launch_act_rht_bf16(x_bf16, m, k, sign_bits, xt_f16, as_stream(stream)));
+}
+
+size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n) {
+  if (m < 0 || k < 0 || n < 0 || k % 32 != 0) return 0;
+  const DensePlan p = tq4::plan_dense(m, k, n);
+  return linear_layout(m, k, n, p).total;
+}
+
+int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed, int64_t n,
+               uint32_t sign_bits, float *y, void *workspace, size_t workspace_bytes,
+               void *stream) {
+  if (m < 0 || k < 0 || n < 0 || k % 32 != 0) return TQ4_E_SHAPE;
+  if (m == 0 || n == 0) return TQ4_OK;
+  if (y == nullptr) return TQ4_E_NULL;
+  if (!aligned(y, 4)) return TQ4_E_ALIGN;
+  hipStream_t s = as_stream(stream);
+  if (k == 0) return device_status(tq4::launch_fill_zero(y, m * n, s));
+  if (x_bf16 == nullptr || packed == nullptr) return TQ4_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(packed, 4)) return TQ4_E_ALIGN;
+  const DensePlan p = tq4::plan_dense(m, k, n);
+  const LinearLayout l = linear_layout(m, k, n, p);
+  if (workspace == nullptr || workspace_bytes < l.total) return TQ4_E_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
+  char *ws = static_cast<char *>(workspace);
+  uint16_t *xt = reinterpret_cast<uint16_t *>(ws + l.xt);
+  int32_t *counters = reinterpret_cast<int32_t *>(ws + l.counters);
+  hipError_t e = tq4::launch_act_rht_bf16(x_bf16, m, k, sign_bits, xt, s, counters,
+                                          static_cast<int64_t>(p.counter_bytes / 4));
+  if (e != hipSuccess) return TQ4_E_DEVICE;
+  e = tq4::launch_dense(p, xt, m, k, packed, n, y, reinterpret_cast<float *>(ws + l.partial),
+                        counters, s);
+  return device_status(e);
+}
+
+int tq4_moe_route(const int32_t *topk_ids, int64_t t, int32_t topk, int32_t n_experts,
+                  int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, void *stream) {
+  if (t < 0 || topk < 1 || n_experts < 1 || n_experts > 512) return TQ4_E_SHAPE;
+  if (t * topk > INT32_MAX) return TQ4_E_SHAPE;
+  if (counts == nullptr || offsets == nullptr) return TQ4_E_NULL;
+  if (t > 0 && (topk_ids == nullptr || perm == nullptr || inv == nullptr)) return TQ4_E_NULL;
+  if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv, 4) ||
+      !aligned(topk_ids, 4))
+    return TQ4_E_ALIGN;
+  // Bucketing only: no tile list is requested (tiles == nullptr).
+  return device_status(tq4::launch_route(topk_ids, t * topk, topk, n_experts, counts, offsets,
+                                         perm, inv, nullptr, nullptr, 0, nullptr,
+                                         as_stream(stream)));
+}
+
+size_t tq4_moe_workspace_size(int64_t t, int32_t topk, int32_t n_experts, int64_t n1, int64_t k) {
+  if (!moe_shape_ok(t, topk, n_experts, n1, k)) return 0;
+  const MoEPlan p = tq4::plan_moe(t * topk, n_experts);
+  return moe_layout(t, topk, n_experts, n1, k, p).total;
+}
+
+int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t *topk_ids,
+                    const float *topk_w, int32_t topk, int32_t n_experts,
+                    const uint8_t *w1_packed, int64_t n1, const uint8_t *w2_packed,
+                    uint32_t sign_bits, float *out, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  if (!moe_shape_ok(t, topk, n_experts, n1, k)) return TQ4_E_SHAPE;
+  if (t == 0) return TQ4_OK;
+  if (x_bf16 == nullptr || topk_ids == nullptr || topk_w == nullptr || w1_packed == nullptr ||
+      w2_packed == nullptr || out == nullptr)
+    return TQ4_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      !aligned(w1_packed, 4) || !aligned(w2_packed, 4) || !aligned(out, 16))
+    return TQ4_E_ALIGN;
+  const MoEPlan p = tq4::plan_moe(t * topk, n_experts);
+  const MoELayout l = moe_layout(t, topk, n_experts, n1, k, p);
+  if (workspace == nullptr || workspace_bytes < l.total) return TQ4_E_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
+
+  char *ws = static_cast<char *>(workspace);
+  int32_t *counts = reinterpret_cast<int32_t *>(ws + l.counts);
+  int32_t *offsets = reinterpret_cast<int32_t *>(ws + l.offsets);
+  int32_t *perm = reinterpret_cast<int32_t *>(ws + l.perm);
+  int32_t *inv = reinterpret_cast<int32_t *>(ws + l.inv);
+  MoETile *tiles = reinterpret_cast<MoETile *>(ws + l.tiles);
+  int32_t *meta = reinterpret_cast<int32_t *>(ws + l.meta);
+  uint16_t *xt = reinterpret_cast<uint16_t *>(ws + l.xt);
+  float *h = reinterpret_cast<float *>(ws + l.h);
+  uint16_t *ht = reinterpret_cast<uint16_t *>(ws + l.ht);
+  float *o = reinterpret_cast<float *>(ws + l.o);
+  const int64_t pairs = t * topk;
+  hipStream_t s = as_stream(stream);
+
+  hipError_t e = tq4::launch_route(topk_ids, pairs, topk, n_experts, counts, offsets, perm, inv,
+                                   tiles, meta, p.tile_rows, nullptr, s);
+  if (e == hipSuccess) e = tq4::launch_act_rht_bf16(x_bf16, t, k, sign_bits, xt, s);
+  if (e == hipSuccess)
+    e = tq4::launch_moe_gemm(p, 0, xt, k, perm, topk, w1_packed, n1, tiles, meta, h, s);
+  if (e == hipSuccess) e = tq4::launch_act_rht_f32(h, pairs, n1, sign_bits, ht, s);
+  if (e == hipSuccess)
+    e = tq4::launch_moe_gemm(p, 1, ht, n1, perm, topk, w2_packed, k, tiles, meta, o, s);
+  if (e == hipSuccess) e = tq4::launch_combine(o, inv, topk_w, t, topk, k, out, s);
+  return device_status(e);
+}
+
+}  // extern "C"

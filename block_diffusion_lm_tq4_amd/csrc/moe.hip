@@ -1,0 +1,181 @@
+// MoE routing and combine for the grouped TQ4_1S layer.
+//
+// Nemotron-TheHobbit-30B-A3B model card: section The model underneath
+// (128-expert MoE, top-6) and section Running it ("sync-free MoE"; the stock
+// loop synchronized host and device many times per token, section
+// Performance & why it's slow).  Everything below stays on the device: the
+// bucketing writes the expert counts, offsets, the stable permutation and the
+// tile list that the grouped products read, and the host never looks at them.
+#include "tq4_internal.h"
+
+namespace tq4 {
+namespace {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kMaxExperts = 512;
+
+// Mask of the lanes (among `active`) whose key equals this lane's key.
+__device__ inline uint64_t same_key_lanes(int key, uint64_t active, int key_bits) {
+  uint64_t m = active;
+  for (int b = 0; b < key_bits; ++b) {
+    const uint64_t ones = __ballot((key >> b) & 1);
+    m &= ((key >> b) & 1) ? ones : ~ones;
+  }
+  return m;
+}
+
+// One workgroup.  Pairs are split into kRouteWaves contiguous ranges, one per
+// wave, walked in batches of 64 in pair order:
+//   pass 1  per-wave expert histograms (LDS);
+//   scan    per expert, over the waves in order, then over the experts;
+//   pass 2  each pair's slot = offsets[e] + (pairs of e in earlier waves)
+//           + (pairs of e earlier in this wave), the last term from ballots.
+// This is a stable counting sort: inside an expert, pairs keep their order.
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const int32_t *__restrict__ ids, int64_t pairs, int32_t n_experts, int32_t *counts,
+    int32_t *offsets, int32_t *perm, int32_t *inv, MoETile *tiles, int32_t *n_tiles,
+    int32_t tile_rows, int32_t *status) {
+  __shared__ int32_t hist[kRouteWaves][kMaxExperts];
+  __shared__ int32_t base[kMaxExperts + 1];
+  __shared__ int32_t tile_base[kMaxExperts + 1];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  int key_bits = 0;
+  while ((1 << key_bits) < n_experts) ++key_bits;
+
+  for (int i = tid; i < kRouteWaves * kMaxExperts; i += kRouteThreads)
+    (&hist[0][0])[i] = 0;
+  __syncthreads();
+
+  const int64_t per_wave = (pairs + kRouteWaves - 1) / kRouteWaves;
+  const int64_t p_begin = wave * per_wave;
+  const int64_t p_end = (p_begin + per_wave < pairs) ? p_begin + per_wave : pairs;
+
+  int32_t bad = 0;
+  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
+    const int64_t p = p0 + lane;
+    const int e = (p < p_end) ? ids[p] : -1;
+    const bool valid = (p < p_end) && e >= 0 && e < n_experts;
+    if (valid) atomicAdd(&hist[wave][e], 1);
+    if (p < p_end && !valid) ++bad;
+  }
+  __syncthreads();
+
+  // per expert: exclusive scan over waves, total count
+  for (int e = tid; e < n_experts; e += kRouteThreads) {
+    int32_t run = 0;
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int32_t c = hist[w][e];
+      hist[w][e] = run;
+      run += c;
+    }
+    counts[e] = run;
+    base[e] = run;
+    tile_base[e] = tile_rows > 0 ? (run + tile_rows - 1) / tile_rows : 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0, trun = 0;
+    for (int e = 0; e < n_experts; ++e) {
+      const int32_t c = base[e], tc = tile_base[e];
+      base[e] = run;
+      tile_base[e] = trun;
+      offsets[e] = run;
+      run += c;
+      trun += tc;
+    }
+    base[n_experts] = run;
+    offsets[n_experts] = run;
+    tile_base[n_experts] = trun;
+    if (n_tiles != nullptr) *n_tiles = trun;
+  }
+  __syncthreads();
+
+  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
+    const int64_t p = p0 + lane;
+    const int e = (p < p_end) ? ids[p] : -1;
+    const bool valid = (p < p_end) && e >= 0 && e < n_experts;
+    const uint64_t active = __ballot(valid);
+    const int key = valid ? e : 0;
+    const uint64_t same = same_key_lanes(key, active, key_bits);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (valid) {
+      const int rank = __popcll(same & below);
+      const int32_t slot = base[e] + hist[wave][e] + rank;
+      perm[slot] = static_cast<int32_t>(p);
+      inv[p] = slot;
+    } else if (p < p_end) {
+      inv[p] = -1;
+    }
+    // the lowest lane of each key group advances the wave's running count
+    if (valid && (same & below) == 0) hist[wave][e] += __popcll(same);
+  }
+
+  // tile list: expert e owns tiles tile_base[e] .. tile_base[e+1]-1
+  for (int e = tid; tiles != nullptr && tile_rows > 0 && e < n_experts; e += kRouteThreads) {
+    const int32_t c = base[e + 1] - base[e];
+    for (int32_t i = 0; i * tile_rows < c; ++i) {
+      MoETile t;
+      t.expert = e;
+      t.row0 = base[e] + i * tile_rows;
+      t.rows = (c - i * tile_rows < tile_rows) ? c - i * tile_rows : tile_rows;
+      t.pad = 0;
+      tiles[tile_base[e] + i] = t;
+    }
+  }
+  if (status != nullptr && bad != 0) atomicAdd(status, bad);
+}
+
+// out[t, :] = sum_j w[t, j] * o[inv[t*topk + j], :] in slot order; each thread
+// owns four consecutive features of one token.
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o,
+                                                      const int32_t *__restrict__ inv,
+                                                      const float *__restrict__ topk_w,
+                                                      int64_t t, int32_t topk, int64_t k,
+                                                      float *__restrict__ out) {
+  const int64_t q = k / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= t * q) return;
+  const int64_t tok = idx / q;
+  const int64_t c = idx % q;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < topk; ++j) {
+    const int32_t row = inv[tok * topk + j];
+    if (row < 0) continue;
+    const float gw = topk_w[tok * topk + j];
+    const float4 v = reinterpret_cast<const float4 *>(o + static_cast<int64_t>(row) * k)[c];
+    s.x += gw * v.x;
+    s.y += gw * v.y;
+    s.z += gw * v.z;
+    s.w += gw * v.w;
+  }
+  reinterpret_cast<float4 *>(out + tok * k)[c] = s;
+}
+
+}  // namespace
+
+hipError_t launch_route(const int32_t *ids, int64_t pairs, int32_t topk, int32_t n_experts,
+                        int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                        MoETile *tiles, int32_t *n_tiles, int32_t tile_rows, int32_t *status,
+                        hipStream_t s) {
+  (void)topk;
+  if (n_experts > kMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, pairs, n_experts,
+                     counts, offsets, perm, inv, tiles, n_tiles, tile_rows, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float *o, const int32_t *inv, const float *topk_w, int64_t t,
+                          int32_t topk, int64_t k, float *out, hipStream_t s) {
+  const int64_t work = t * (k / 4);
+  if (work == 0) return hipSuccess;
+  const int threads = 256;
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((work + threads - 1) / threads)),
+                     dim3(threads), 0, s, o, inv, topk_w, t, topk, k, out);
+  return hipGetLastError();
+}
+
+}  // namespace tq4

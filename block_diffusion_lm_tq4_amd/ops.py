@@ -1,0 +1,164 @@
+"""Torch-facing binding of the TQ4_1S C ABI: argument marshalling only.
+
+Every function takes device tensors, checks dtypes and shapes, and passes raw
+pointers, sizes and the current HIP stream to libtq4.so.  All arithmetic runs
+in the library's kernels; torch only provides memory and streams.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import check, lib
+
+BLOCK = 32
+BLOCK_BYTES = 20
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _cuda_contig(t: torch.Tensor, name: str, dtype) -> None:
+    _require(t.is_cuda, f"{name} must be a device tensor")
+    _require(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+class Workspace:
+    """Grow-only device scratch buffers, one per (device, purpose)."""
+
+    def __init__(self):
+        self._bufs: dict = {}
+
+    def get(self, device: torch.device, key: str, nbytes: int) -> torch.Tensor:
+        k = (str(device), key)
+        buf = self._bufs.get(k)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._bufs[k] = buf
+        return buf
+
+
+_WS = Workspace()
+
+
+def codebook() -> torch.Tensor:
+    """The 16 stored levels (fp32, CPU tensor), as the library computes them."""
+    out = torch.empty(16, dtype=torch.float32)
+    check("tq4_codebook", lib().tq4_codebook(out.data_ptr()))
+    return out
+
+
+def packed_size(n: int, k: int) -> int:
+    return int(lib().tq4_packed_size(n, k))
+
+
+def pack(w: torch.Tensor, sign_bits: int, nonfinite: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 W [n, k] -> packed uint8 [n, k/32, 20] (tq4_pack)."""
+    _cuda_contig(w, "w", torch.float32)
+    _require(w.dim() == 2 and w.shape[1] % BLOCK == 0, "w must be [n, k] with k % 32 == 0")
+    n, k = w.shape
+    out = torch.empty((n, k // BLOCK, BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    if nonfinite is not None:
+        _cuda_contig(nonfinite, "nonfinite", torch.int32)
+    check("tq4_pack", lib().tq4_pack(w.data_ptr(), n, k, sign_bits & 0xFFFFFFFF, out.data_ptr(),
+                                     _ptr(nonfinite), _stream(w.device)))
+    return out
+
+
+def act_rht(x: torch.Tensor, sign_bits: int) -> torch.Tensor:
+    """bf16 x [m, k] -> fp16 R x per 32-block (tq4_act_rht)."""
+    _cuda_contig(x, "x", torch.bfloat16)
+    m, k = x.shape
+    out = torch.empty((m, k), dtype=torch.float16, device=x.device)
+    check("tq4_act_rht", lib().tq4_act_rht(x.data_ptr(), m, k, sign_bits & 0xFFFFFFFF,
+                                           out.data_ptr(), _stream(x.device)))
+    return out
+
+
+def linear_workspace_size(m: int, k: int, n: int) -> int:
+    return int(lib().tq4_linear_workspace_size(m, k, n))
+
+
+def linear(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x . W_hat^T, fp32 [m, n] (tq4_linear)."""
+    _cuda_contig(x, "x", torch.bfloat16)
+    _cuda_contig(packed, "packed", torch.uint8)
+    _require(x.dim() == 2, "x must be [m, k]")
+    m, k = x.shape
+    _require(packed.dim() == 3 and packed.shape[1] * BLOCK == k and packed.shape[2] == BLOCK_BYTES,
+             "packed must be [n, k/32, 20]")
+    n = packed.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _cuda_contig(out, "out", torch.float32)
+    _require(tuple(out.shape) == (m, n), "out must be [m, n]")
+    need = linear_workspace_size(m, k, n)
+    if workspace is None:
+        workspace = _WS.get(x.device, "linear", need)
+    check("tq4_linear", lib().tq4_linear(x.data_ptr(), m, k, packed.data_ptr(), n,
+                                         sign_bits & 0xFFFFFFFF, out.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel(),
+                                         _stream(x.device)))
+    return out
+
+
+def moe_route(topk_ids: torch.Tensor, n_experts: int):
+    """Stable bucketing of (token, slot) pairs by expert (tq4_moe_route)."""
+    _cuda_contig(topk_ids, "topk_ids", torch.int32)
+    t, topk = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    perm = torch.full((t * topk,), -7, dtype=torch.int32, device=dev)
+    inv = torch.empty(t * topk, dtype=torch.int32, device=dev)
+    check("tq4_moe_route", lib().tq4_moe_route(topk_ids.data_ptr(), t, topk, n_experts,
+                                               counts.data_ptr(), offsets.data_ptr(),
+                                               perm.data_ptr(), inv.data_ptr(), _stream(dev)))
+    return counts, offsets, perm, inv
+
+
+def moe_workspace_size(t: int, topk: int, n_experts: int, n1: int, k: int) -> int:
+    return int(lib().tq4_moe_workspace_size(t, topk, n_experts, n1, k))
+
+
+def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                w1_packed: torch.Tensor, w2_packed: torch.Tensor, sign_bits: int,
+                out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The TQ4_1S MoE layer (tq4_moe_grouped); fp32 [t, k]."""
+    _cuda_contig(x, "x", torch.bfloat16)
+    _cuda_contig(topk_ids, "topk_ids", torch.int32)
+    _cuda_contig(topk_w, "topk_w", torch.float32)
+    _cuda_contig(w1_packed, "w1_packed", torch.uint8)
+    _cuda_contig(w2_packed, "w2_packed", torch.uint8)
+    t, k = x.shape
+    _require(topk_ids.dim() == 2 and topk_ids.shape[0] == t, "topk_ids must be [t, topk]")
+    topk = topk_ids.shape[1]
+    _require(tuple(topk_w.shape) == (t, topk), "topk_w must be [t, topk]")
+    e, n1, kb1, bb = w1_packed.shape
+    _require(kb1 * BLOCK == k and bb == BLOCK_BYTES, "w1_packed must be [E, n1, k/32, 20]")
+    _require(tuple(w2_packed.shape) == (e, k, n1 // BLOCK, BLOCK_BYTES),
+             "w2_packed must be [E, k, n1/32, 20]")
+    if out is None:
+        out = torch.empty((t, k), dtype=torch.float32, device=x.device)
+    _cuda_contig(out, "out", torch.float32)
+    need = moe_workspace_size(t, topk, e, n1, k)
+    if workspace is None:
+        workspace = _WS.get(x.device, "moe", need)
+    check("tq4_moe_grouped", lib().tq4_moe_grouped(
+        x.data_ptr(), t, k, topk_ids.data_ptr(), topk_w.data_ptr(), topk, e,
+        w1_packed.data_ptr(), n1, w2_packed.data_ptr(), sign_bits & 0xFFFFFFFF,
+        out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x.device)))
+    return out

@@ -1,0 +1,164 @@
+/*
+ * tq4.h -- C ABI of the TQ4_1S ("Config-I") dequantize-and-multiply library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Format (Nemotron-TheHobbit-30B-A3B model card, section What "Config-I"
+ * means: a Walsh-Hadamard rotation per 32-weight block, a 16-level Lloyd-Max
+ * codebook, two half-block scales, about 5 bits per weight).  The details the
+ * card leaves open are fixed here as follows:
+ *   - a block is 32 consecutive input features (k) of one output row n;
+ *   - z = H32 (s .* w) / sqrt(32): s_i = -1 where bit i of sign_bits is set,
+ *     H32 is the Sylvester-ordered Hadamard matrix H[i][j] = (-1)^popcount(i&j);
+ *     one sign vector serves every block of every tensor;
+ *   - codebook c_0 < ... < c_15: the 16-level Lloyd-Max quantizer of N(0,1),
+ *     stored as fp32 (tq4_codebook);
+ *   - per half-block h (z elements 0-15, 16-31): S_h = bf16(fp32(max|z| / c_15)),
+ *     both roundings to nearest-even;
+ *   - code q_j = #{k in 0..14 : z_j > S_h * (c_k + c_{k+1}) / 2}, evaluated in
+ *     fp64 (a value exactly on a midpoint takes the lower code);
+ *   - block bytes: 16 code bytes (byte i = q_{2i} | q_{2i+1} << 4), then the
+ *     bf16 bit patterns of S_0 and S_1, little-endian: 20 bytes per block;
+ *     a packed matrix is [n][k/32][20], row-major, contiguous.
+ *
+ * Conventions for every entry point below:
+ *   - Pointers named as device pointers are device memory owned by the caller;
+ *     the library never frees them.  Host pointers are named as such.
+ *   - All GPU work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and nothing waits on the host: outputs are ready when the stream
+ *     reaches that point.  The library never allocates device memory; the
+ *     calls that need scratch space take a caller-provided workspace.
+ *   - Argument errors are reported synchronously by the return value before
+ *     any GPU work is enqueued.  A failed launch returns TQ4_E_DEVICE.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Two calls that share a workspace must not run concurrently.
+ */
+#ifndef TQ4_H
+#define TQ4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ4_BLOCK 32        /* weights per block, along k                  */
+#define TQ4_BLOCK_BYTES 20  /* 16 code bytes + two bf16 half-block scales  */
+#define TQ4_LEVELS 16
+
+typedef enum {
+  TQ4_OK = 0,
+  TQ4_E_NULL = 1,        /* a required pointer is NULL                          */
+  TQ4_E_SHAPE = 2,       /* a size is out of range (k % 32 != 0, topk > E, ...) */
+  TQ4_E_ALIGN = 3,       /* a pointer is not aligned as its argument requires   */
+  TQ4_E_WORKSPACE = 4,   /* workspace NULL or smaller than the size query says  */
+  TQ4_E_DEVICE = 5       /* a HIP call or kernel launch failed                  */
+} tq4_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *tq4_status_string(int status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int tq4_version(void);
+
+/* Host-only (no GPU call): writes the 16 stored codebook levels, ascending, to
+ * the host array out[16].  The levels are the 16-level Lloyd-Max quantizer of
+ * N(0,1) (model card, What "Config-I" means: "16-level Lloyd-Max") rounded to
+ * fp32.  Returns TQ4_E_NULL if out is NULL. */
+int tq4_codebook(float *out);
+
+/* Bytes of a packed [n, k] matrix: n * (k/32) * 20; 0 if n < 0, k < 0 or
+ * k % 32 != 0. */
+size_t tq4_packed_size(int64_t n, int64_t k);
+
+/* Encode W (fp32, [n, k] row-major, device, 16-byte aligned) into `packed`
+ * (device, [n][k/32][20], 4-byte aligned).  Model card, What "Config-I"
+ * means (rotation, codebook, dual half-block scales); offline quantizer of
+ * section Reproduction.  All arithmetic is fp64, so the codes are exactly
+ * those of the rule in the header comment.  `nonfinite_count` (device int32,
+ * optional): increased by the number of blocks holding a NaN or infinity;
+ * such blocks are still encoded by the same IEEE rule.
+ * Errors: TQ4_E_NULL (w/packed NULL with n*k > 0), TQ4_E_SHAPE (n < 0, k < 0,
+ * k % 32 != 0), TQ4_E_ALIGN, TQ4_E_DEVICE.  n == 0 or k == 0 is a no-op. */
+int tq4_pack(const float *w, int64_t n, int64_t k, uint32_t sign_bits,
+             uint8_t *packed, int32_t *nonfinite_count, void *stream);
+
+/* Rotate activations per 32-block: xt[m, :] = R x[m, :] with
+ * R = H32 diag(s) / sqrt(32) on each block, fp32 arithmetic, result rounded to
+ * fp16.  x: bf16 bit patterns [m, k] (device, 16-byte aligned); xt: fp16 bit
+ * patterns [m, k] (device, 16-byte aligned).  Because R is orthogonal,
+ * x . W_hat^T = (R x) . Z_hat^T blockwise, where Z_hat holds S_h * c_q: the
+ * rotation moves from the weights to the activations.  Errors as tq4_pack. */
+int tq4_act_rht(const uint16_t *x_bf16, int64_t m, int64_t k, uint32_t sign_bits,
+                uint16_t *xt_f16, void *stream);
+
+/* Workspace bytes tq4_linear needs for these sizes (0 if the sizes are
+ * invalid).  No initial contents are required. */
+size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n);
+
+/* The on-the-fly dequantizing linear layer (model card, section Running it):
+ * y[m, n] = sum_k x[m, k] * W_hat[n, k], W_hat the decoded packed weights,
+ * without bias or activation.
+ *   x_bf16  : [m, k] bf16 bit patterns, device, 16-byte aligned
+ *   packed  : [n][k/32][20], device, 4-byte aligned (from tq4_pack)
+ *   y       : [m, n] fp32, device, 4-byte aligned, overwritten
+ *   workspace / workspace_bytes : device scratch of at least
+ *             tq4_linear_workspace_size(m, k, n) bytes, 256-byte aligned
+ * The rotation is applied to the activations (tq4_act_rht) and the product
+ * runs on 16-bit MFMA with fp32 accumulation; results are deterministic.
+ * Errors: TQ4_E_NULL, TQ4_E_SHAPE (negative sizes, k % 32 != 0),
+ * TQ4_E_ALIGN, TQ4_E_WORKSPACE, TQ4_E_DEVICE.  m == 0 or n == 0 is a no-op;
+ * k == 0 writes zeros. */
+int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k,
+               const uint8_t *packed, int64_t n, uint32_t sign_bits, float *y,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Stable bucketing of the t*topk (token, slot) pairs by expert, the routing
+ * step of the sync-free MoE (model card, Running it; 128 experts, top-6 in
+ * The model underneath).  Pair p = token * topk + slot.
+ *   topk_ids : [t, topk] int32, device
+ *   counts   : [n_experts] int32, device  -- pairs per expert
+ *   offsets  : [n_experts + 1] int32, device -- exclusive prefix of counts
+ *   perm     : [t * topk] int32, device  -- perm[offsets[e] + r] is the r-th
+ *              pair (in increasing p) routed to e; entries past offsets[E]
+ *              are left untouched
+ *   inv      : [t * topk] int32, device  -- inv[perm[i]] = i; -1 for pairs
+ *              whose id is outside [0, n_experts)
+ * One kernel, no host synchronization.  Errors: TQ4_E_NULL, TQ4_E_SHAPE
+ * (t < 0, topk < 1, n_experts < 1 or > 512), TQ4_E_DEVICE. */
+int tq4_moe_route(const int32_t *topk_ids, int64_t t, int32_t topk, int32_t n_experts,
+                  int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                  void *stream);
+
+/* Workspace bytes tq4_moe_grouped needs (0 if the sizes are invalid). */
+size_t tq4_moe_workspace_size(int64_t t, int32_t topk, int32_t n_experts,
+                              int64_t n1, int64_t k);
+
+/* The MoE layer on TQ4_1S experts, without host synchronization (model card,
+ * Running it: "sync-free MoE"; The model underneath: 128 experts, top-6):
+ *   out[t, :] = sum_j topk_w[t, j] * relu(x[t, :] . W1_e^T)^2 . W2_e^T,
+ *   e = topk_ids[t, j]; ids outside [0, n_experts) contribute nothing.
+ *   x_bf16    : [t, k] bf16 bit patterns, device, 16-byte aligned
+ *   topk_ids  : [t, topk] int32, device;  topk_w : [t, topk] fp32, device
+ *   w1_packed : [n_experts][n1][k/32][20] (up projections), device
+ *   w2_packed : [n_experts][k][n1/32][20] (down projections), device
+ *   out       : [t, k] fp32, device, overwritten
+ *   workspace : at least tq4_moe_workspace_size(...) bytes, device,
+ *               256-byte aligned; no initial contents required
+ * Steps: bucketing (tq4_moe_route), activation rotation, grouped up
+ * projection with relu^2, rotation of the hidden rows, grouped down
+ * projection, and a per-token weighted sum over the top-k slots in slot
+ * order (deterministic).  Errors: TQ4_E_NULL, TQ4_E_SHAPE (k or n1 not a
+ * multiple of 32, topk > n_experts, ...), TQ4_E_ALIGN, TQ4_E_WORKSPACE,
+ * TQ4_E_DEVICE.  t == 0 is a no-op. */
+int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k,
+                    const int32_t *topk_ids, const float *topk_w, int32_t topk,
+                    int32_t n_experts, const uint8_t *w1_packed, int64_t n1,
+                    const uint8_t *w2_packed, uint32_t sign_bits, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ4_H */

@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from block_diffusion_lm_tq4_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq4.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_WS = 0, 1, 2, 3, 4
+FAKE = 0x10000          # a non-null, 256-byte aligned address that is never touched
+MIS = FAKE + 2          # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libtq4.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version(L):
+    for s in range(6):
+        assert L.tq4_status_string(s)
+    assert L.tq4_status_string(99) == b"unknown status"
+    assert L.tq4_version() >= 100
+
+
+def test_codebook_equals_oracle_bit_for_bit(L):
+    out = (ctypes.c_float * 16)()
+    assert L.tq4_codebook(ctypes.addressof(out)) == OK
+    lib_cb = np.frombuffer(out, dtype=np.float32)
+    assert np.array_equal(lib_cb.view(np.uint32), O.codebook().view(np.uint32))
+    assert L.tq4_codebook(None) == E_NULL
+
+
+def test_packed_size(L):
+    assert L.tq4_packed_size(8192, 2688) == 13762560
+    assert L.tq4_packed_size(512, 256) == 81920
+    assert L.tq4_packed_size(3, 33) == 0
+    assert L.tq4_packed_size(-1, 32) == 0
+    assert L.tq4_packed_size(0, 64) == 0
+
+
+def test_pack_argument_errors(L):
+    assert L.tq4_pack(FAKE, 4, 33, 0, FAKE, None, None) == E_SHAPE
+    assert L.tq4_pack(FAKE, -1, 32, 0, FAKE, None, None) == E_SHAPE
+    assert L.tq4_pack(None, 4, 32, 0, FAKE, None, None) == E_NULL
+    assert L.tq4_pack(FAKE, 4, 32, 0, None, None, None) == E_NULL
+    assert L.tq4_pack(FAKE + 4, 4, 32, 0, FAKE, None, None) == E_ALIGN
+    assert L.tq4_pack(FAKE, 4, 32, 0, FAKE + 1, None, None) == E_ALIGN
+    assert L.tq4_pack(FAKE, 4, 32, 0, FAKE, FAKE + 2, None) == E_ALIGN
+    assert L.tq4_pack(None, 0, 32, 0, None, None, None) == OK      # empty: no-op
+
+
+def test_act_rht_argument_errors(L):
+    assert L.tq4_act_rht(FAKE, 4, 40, 0, FAKE, None) == E_SHAPE
+    assert L.tq4_act_rht(None, 4, 32, 0, FAKE, None) == E_NULL
+    assert L.tq4_act_rht(MIS, 4, 32, 0, FAKE, None) == E_ALIGN
+    assert L.tq4_act_rht(None, 0, 32, 0, None, None) == OK
+
+
+def test_linear_argument_errors(L):
+    ws = L.tq4_linear_workspace_size(16, 2688, 8192)
+    assert ws > 16 * 2688 * 2
+    assert L.tq4_linear_workspace_size(16, 33, 8) == 0
+    args = dict(x=FAKE, m=16, k=2688, p=FAKE, n=8192, sb=0, y=FAKE, ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.tq4_linear(a["x"], a["m"], a["k"], a["p"], a["n"], a["sb"], a["y"], a["ws"],
+                            a["wsb"], None)
+
+    assert call(k=2690) == E_SHAPE
+    assert call(m=-1) == E_SHAPE
+    assert call(x=None) == E_NULL
+    assert call(p=None) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(x=MIS) == E_ALIGN
+    assert call(p=FAKE + 2) == E_ALIGN
+    assert call(y=FAKE + 2) == E_ALIGN
+    assert call(ws=None) == E_WS
+    assert call(wsb=ws - 1) == E_WS
+    assert call(ws=FAKE + 16) == E_ALIGN
+    assert call(m=0) == OK and call(n=0) == OK      # empty output: no-op
+
+
+def test_moe_argument_errors(L):
+    ws = L.tq4_moe_workspace_size(16, 6, 128, 1856, 2688)
+    assert ws > 0
+    assert L.tq4_moe_workspace_size(16, 6, 128, 1850, 2688) == 0     # n1 % 32
+    assert L.tq4_moe_workspace_size(16, 7, 4, 64, 64) == 0           # topk > E
+    assert L.tq4_moe_workspace_size(16, 6, 513, 64, 64) == 0         # E too large
+    a = [FAKE, 16, 2688, FAKE, FAKE, 6, 128, FAKE, 1856, FAKE, 0, FAKE, FAKE, ws, None]
+
+    def call(i=None, v=None):
+        b = list(a)
+        if i is not None:
+            b[i] = v
+        return L.tq4_moe_grouped(*b)
+
+    assert call(2, 2689) == E_SHAPE
+    assert call(5, 0) == E_SHAPE
+    assert call(0, None) == E_NULL
+    assert call(3, None) == E_NULL
+    assert call(7, None) == E_NULL
+    assert call(0, MIS) == E_ALIGN
+    assert call(11, FAKE + 4) == E_ALIGN
+    assert call(12, None) == E_WS
+    assert call(13, ws - 1) == E_WS
+    assert call(1, 0) == OK                                           # t == 0: no-op
+
+
+def test_route_argument_errors(L):
+    assert L.tq4_moe_route(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert L.tq4_moe_route(FAKE, 4, 2, 600, FAKE, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert L.tq4_moe_route(FAKE, 4, 2, 8, None, FAKE, FAKE, FAKE, None) == E_NULL
+    assert L.tq4_moe_route(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, None) == E_NULL
+    assert L.tq4_moe_route(FAKE, 4, 2, 8, FAKE, FAKE + 1, FAKE, FAKE, None) == E_ALIGN
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.lib()

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Bars: packed bytes and integer bucketing bit-exact; products within
+relative Frobenius error <= 2e-3 and max |err| <= 1e-2 * rms(y_ref).
+Full-size workloads compare every output where the oracle finishes in
+seconds and sampled rows/tokens elsewhere.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from block_diffusion_lm_tq4_amd import inputs as I
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+SB = I.sign_bits()
+REL_F = 2e-3
+MAX_REL_RMS = 1e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_lm_tq4_amd import ops  # noqa: F401  (loads libtq4.so)
+    return torch.device("cuda:0")
+
+
+def _ops():
+    from block_diffusion_lm_tq4_amd import ops
+    return ops
+
+
+def _bf16(x_bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def _check_close(y, ref, what=""):
+    y = np.asarray(y, dtype=np.float64)
+    err = y - ref
+    nref = np.linalg.norm(ref)
+    relf = np.linalg.norm(err) / nref if nref > 0 else np.linalg.norm(err)
+    rms = np.sqrt(np.mean(ref * ref))
+    mx = np.max(np.abs(err)) if err.size else 0.0
+    print(f"{what}: relF={relf:.3e} max/rms={mx / max(rms, 1e-300):.3e}")
+    assert relf <= REL_F, (what, relf)
+    assert mx <= MAX_REL_RMS * rms, (what, mx, rms)
+
+
+# ----------------------------------------------------------------------------- pack
+
+@pytest.mark.parametrize("n,k,kind", [
+    (512, 256, "gaussian"),          # 512x256 layer
+    (8192, 2688, "gaussian"),        # dense denoiser projection
+    (8192, 2688, "student_t3"),      # heavy-tailed prefill projection
+    (3, 32, "gaussian"),
+    (1, 2688, "student_t3"),
+    (37, 96, "gaussian"),
+])
+def test_pack_bytes_equal_oracle(dev, n, k, kind):
+    w = I.weights(n, k, kind)
+    got = _ops().pack(torch.from_numpy(w).to(dev), SB).cpu().numpy()
+    want = O.pack(w, SB)
+    assert got.shape == want.shape
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first at {bad[:5].tolist()}"
+
+
+def test_pack_moe_experts_equal_oracle(experts):
+    """All 128 experts' up and down projections, byte for byte."""
+    _, _, _, mismatched = experts
+    assert mismatched == []
+
+
+def test_pack_special_blocks(dev):
+    w = np.zeros((6, 64), dtype=np.float32)
+    w[1, 7] = 1.0                                   # one-hot block
+    w[2, :] = 0.5                                   # constant row
+    w[3, 40] = -3e-3
+    w[4, :32] = np.float32(1e-30)                   # tiny values
+    rng = np.random.default_rng(1)
+    w[5] = rng.standard_normal(64).astype(np.float32) * 1e4
+    got = _ops().pack(torch.from_numpy(w).to(dev), SB).cpu().numpy()
+    assert np.array_equal(got, O.pack(w, SB))
+
+
+def test_pack_nonfinite_counted(dev):
+    w = I.weights(4, 96)
+    w[1, 5] = np.nan
+    w[3, 70] = np.inf
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    got = _ops().pack(torch.from_numpy(w).to(dev), SB, nonfinite=cnt).cpu().numpy()
+    assert int(cnt.item()) == 2
+    assert np.array_equal(got, O.pack(w, SB))
+
+
+def test_pack_sign_bits_matter(dev):
+    w = I.weights(16, 64)
+    for sb in (0, 0xFFFFFFFF, 0x80000001):
+        got = _ops().pack(torch.from_numpy(w).to(dev), sb).cpu().numpy()
+        assert np.array_equal(got, O.pack(w, sb)), hex(sb)
+
+
+# ----------------------------------------------------------------------- rotation
+
+def test_act_rht_matches_oracle_rotation(dev):
+    x = I.activations_bf16(33, 2688)
+    got = _ops().act_rht(_bf16(x, dev), SB).cpu().numpy().astype(np.float64)
+    want = O.rotate_blocks(O.f64_from_bf16_bits(x).reshape(33, -1, 32), SB).reshape(33, -1)
+    # fp16 rounding of the result: |err| <= 2^-11 |v| (normal range)
+    assert np.all(np.abs(got - want) <= 2.0 ** -11 * np.abs(want) + 2.0 ** -24)
+
+
+# ------------------------------------------------------------------------- linear
+
+def _linear_case(dev, m, k, n, kind="gaussian", wseed=0, xseed=2):
+    w = I.weights(n, k, kind, seed=wseed)
+    x = I.activations_bf16(m, k, seed=xseed)
+    p_ref = O.pack(w, SB)
+    p_gpu = _ops().pack(torch.from_numpy(w).to(dev), SB)
+    y = _ops().linear(_bf16(x, dev), p_gpu, SB)
+    torch.cuda.synchronize()
+    return x, p_ref, y.cpu().numpy()
+
+
+def test_linear_512x256_m16(dev):
+    x, p, y = _linear_case(dev, 16, 256, 512)
+    _check_close(y, O.linear(x, p, SB), "linear 16x256x512")
+
+
+def test_linear_dense_m16_full(dev):
+    x, p, y = _linear_case(dev, 16, 2688, 8192)
+    _check_close(y, O.linear(x, p, SB), "linear 16x2688x8192")
+
+
+@pytest.mark.parametrize("m,k,n", [
+    (1, 32, 1), (1, 2688, 8192), (5, 96, 17), (16, 160, 129), (17, 64, 300),
+    (33, 2688, 100), (64, 512, 256), (65, 256, 130), (100, 96, 77), (128, 2688, 256),
+    (200, 1856, 300), (3, 4096, 64),
+])
+def test_linear_ragged_shapes(dev, m, k, n):
+    x, p, y = _linear_case(dev, m, k, n, wseed=m * 7 + n)
+    _check_close(y, O.linear(x, p, SB), f"linear {m}x{k}x{n}")
+
+
+def test_linear_prefill_m4096_sampled_rows(dev):
+    m, k, n = 4096, 2688, 8192
+    x, p, y = _linear_case(dev, m, k, n, kind="student_t3")
+    rows = np.unique(np.concatenate([np.arange(0, m, 97), [m - 1]]))
+    ref = O.linear(x[rows], p, SB)
+    _check_close(y[rows], ref, "linear 4096x2688x8192 (sampled rows)")
+    # property at full size: no NaN/Inf and the output scale matches
+    assert np.isfinite(y).all()
+
+
+def test_linear_identity_rows_read_the_weights(dev):
+    k, n = 96, 64
+    w = I.weights(n, k)
+    eye = np.zeros((k, k), dtype=np.uint16)
+    eye[np.arange(k), np.arange(k)] = 0x3F80
+    p_gpu = _ops().pack(torch.from_numpy(w).to(dev), SB)
+    y = _ops().linear(_bf16(eye, dev), p_gpu, SB).cpu().numpy()
+    _check_close(y, O.dequant(O.pack(w, SB), SB).T, "identity rows")
+
+
+def test_linear_deterministic(dev):
+    w = I.weights(8192, 2688)
+    x = _bf16(I.activations_bf16(16, 2688), dev)
+    p = _ops().pack(torch.from_numpy(w).to(dev), SB)
+    a = _ops().linear(x, p, SB).clone()
+    b = _ops().linear(x, p, SB).clone()
+    assert torch.equal(a, b)
+
+
+def test_linear_workspace_reuse_across_shapes(dev):
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev).fill_(0xAB)
+    for (m, k, n) in [(16, 2688, 8192), (5, 256, 640), (16, 2688, 8192), (40, 512, 4096)]:
+        w = I.weights(n, k, seed=n)
+        x = I.activations_bf16(m, k)
+        p = _ops().pack(torch.from_numpy(w).to(dev), SB)
+        y = _ops().linear(_bf16(x, dev), p, SB, workspace=ws).cpu().numpy()
+        _check_close(y, O.linear(x, O.pack(w, SB), SB), f"ws reuse {m}x{k}x{n}")
+
+
+def test_linear_k0_writes_zeros(dev):
+    x = torch.empty((4, 0), dtype=torch.bfloat16, device=dev)
+    p = torch.empty((8, 0, 20), dtype=torch.uint8, device=dev)
+    y = torch.full((4, 8), 7.0, device=dev)
+    _ops().linear(x, p, SB, out=y)
+    assert not y.any()
+
+
+# ---------------------------------------------------------------------------- MoE
+
+@pytest.fixture(scope="module")
+def experts(dev):
+    """GPU-packed expert stacks for the 128-expert layer, plus the oracle's own
+    packing of every expert (computed on the CPU in threads) and the list of
+    experts whose GPU bytes differ from it."""
+    from concurrent.futures import ThreadPoolExecutor
+    n_exp, n1, k = 128, 1856, 2688
+    w1 = torch.empty((n_exp, n1, k // 32, 20), dtype=torch.uint8, device=dev)
+    w2 = torch.empty((n_exp, k, n1 // 32, 20), dtype=torch.uint8, device=dev)
+    ref, bad = {}, []
+
+    def work(e):
+        a, b = I.expert_weights(e, 1, n1, k), I.expert_weights(e, 2, n1, k)
+        return e, a, b, O.pack(a, SB), O.pack(b, SB)
+
+    with ThreadPoolExecutor(8) as ex:
+        for lo in range(0, n_exp, 16):
+            for e, a, b, pa, pb in ex.map(work, range(lo, min(lo + 16, n_exp))):
+                w1[e] = _ops().pack(torch.from_numpy(a).to(dev), SB)
+                w2[e] = _ops().pack(torch.from_numpy(b).to(dev), SB)
+                if not (np.array_equal(w1[e].cpu().numpy(), pa)
+                        and np.array_equal(w2[e].cpu().numpy(), pb)):
+                    bad.append(e)
+                ref[e] = (pa, pb)
+    return w1, w2, ref, bad
+
+
+def _oracle_expert(experts, which):
+    ref = experts[2]
+    return lambda e: ref[int(e)][which - 1]
+
+
+@pytest.mark.parametrize("name", ["moe_t16", "moe_t1024_uniform", "moe_t1024_zipf"])
+def test_route_bit_exact(dev, name):
+    wl = I.WORKLOADS[name]
+    ids, _ = I.moe_routing(wl)
+    counts, offsets, perm, inv = _ops().moe_route(torch.from_numpy(ids).to(dev), wl.n_experts)
+    c, o, p, iv = O.bucket_pairs(ids, wl.n_experts)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(perm.cpu().numpy()[: p.size], p)
+    assert np.array_equal(inv.cpu().numpy(), iv)
+
+
+def test_route_invalid_ids_and_small_expert_counts(dev):
+    rng = np.random.default_rng(3)
+    for t, e, k in ((1, 1, 1), (7, 3, 2), (300, 128, 6), (5000, 512, 4), (64, 8, 8)):
+        ids = rng.integers(-2, e + 2, size=(t, k)).astype(np.int32)
+        counts, offsets, perm, inv = _ops().moe_route(torch.from_numpy(ids).to(dev), e)
+        c, o, p, iv = O.bucket_pairs(ids, e)
+        assert np.array_equal(counts.cpu().numpy(), c)
+        assert np.array_equal(offsets.cpu().numpy(), o)
+        assert np.array_equal(perm.cpu().numpy()[: p.size], p)
+        assert np.array_equal(inv.cpu().numpy(), iv)
+
+
+def test_moe_t16_full(dev, experts):
+    wl = I.WORKLOADS["moe_t16"]
+    ids, g = I.moe_routing(wl)
+    x = I.activations_bf16(wl.t, wl.k)
+    out = _ops().moe_grouped(_bf16(x, dev), torch.from_numpy(ids).to(dev),
+                             torch.from_numpy(g).to(dev), experts[0], experts[1], SB).cpu().numpy()
+    ref = O.moe(x, ids, g, _oracle_expert(experts, 1), _oracle_expert(experts, 2), SB)
+    _check_close(out, ref, "moe t16")
+
+
+@pytest.mark.parametrize("name", ["moe_t1024_uniform", "moe_t1024_zipf"])
+def test_moe_t1024_sampled_tokens(dev, experts, name):
+    wl = I.WORKLOADS[name]
+    ids, g = I.moe_routing(wl)
+    x = I.activations_bf16(wl.t, wl.k)
+    out = _ops().moe_grouped(_bf16(x, dev), torch.from_numpy(ids).to(dev),
+                             torch.from_numpy(g).to(dev), experts[0], experts[1], SB).cpu().numpy()
+    assert np.isfinite(out).all()
+    # tokens routed to the hottest expert plus a spread sample
+    hot = np.bincount(ids.reshape(-1), minlength=128).argmax()
+    tok = np.unique(np.concatenate([np.nonzero((ids == hot).any(1))[0][:4],
+                                    np.arange(0, wl.t, 97), [wl.t - 1]]))
+    ref = O.moe(x, ids, g, _oracle_expert(experts, 1), _oracle_expert(experts, 2), SB,
+                tokens=tok)
+    _check_close(out[tok], ref, name + " (sampled tokens)")
+
+
+def test_moe_deterministic(dev, experts):
+    wl = I.WORKLOADS["moe_t1024_zipf"]
+    ids, g = I.moe_routing(wl)
+    x = _bf16(I.activations_bf16(wl.t, wl.k), dev)
+    idt, gt = torch.from_numpy(ids).to(dev), torch.from_numpy(g).to(dev)
+    a = _ops().moe_grouped(x, idt, gt, experts[0], experts[1], SB).clone()
+    b = _ops().moe_grouped(x, idt, gt, experts[0], experts[1], SB).clone()
+    assert torch.equal(a, b)
+
+
+def test_moe_small_shapes_and_invalid_ids(dev):
+    rng = np.random.default_rng(11)
+    for (t, e, k, n1, topk) in ((1, 4, 32, 32, 1), (9, 8, 64, 96, 3), (40, 16, 96, 64, 4),
+                                (300, 8, 64, 32, 2)):
+        w1 = (0.05 * rng.standard_normal((e, n1, k))).astype(np.float32)
+        w2 = (0.05 * rng.standard_normal((e, k, n1))).astype(np.float32)
+        p1 = np.stack([O.pack(w1[i], SB) for i in range(e)])
+        p2 = np.stack([O.pack(w2[i], SB) for i in range(e)])
+        x = I.activations_bf16(t, k, seed=t)
+        ids, g = I.route(rng.standard_normal((t, e)), topk)
+        ids = ids.copy()
+        ids[0, 0] = -1                      # dropped slot
+        out = _ops().moe_grouped(_bf16(x, dev), torch.from_numpy(ids).to(dev),
+                                 torch.from_numpy(g).to(dev), torch.from_numpy(p1).to(dev),
+                                 torch.from_numpy(p2).to(dev), SB).cpu().numpy()
+        _check_close(out, O.moe(x, ids, g, list(p1), list(p2), SB), f"moe t{t} e{e}")
