@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Throughput of the TQ4_1S dequantize-and-multiply path on one MI355X.
+
+Headline (`value`): packed-weight GB/s of one dense denoiser-step projection,
+M=16 tokens (one 16-token diffusion block), K=2688, N=8192, through
+tq4_linear (activation rotation + dequant-GEMM).  A step is one such call;
+the weights rotate over `--copies` distinct packed copies (48 x 13.76 MB =
+660 MB, more than twice the 256 MB Infinity Cache), so every step streams
+its weights from HBM.  Inputs are resident in HBM before timing starts.
+
+Extra legs in the same JSON line: the M=4096 prefill projection (TFLOP/s,
+Student-t weights) and the 128-expert top-6 MoE layer at 16 and 1024 tokens
+(uniform and Zipf routing), each timed the same way, with its own roofline.
+
+`roofline` is for the dominant kernel of the headline step, the dequant-GEMM
+(timed alone through tq4_linear_rotated with HIP events on the launch
+stream).  `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
+same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|none|a,b]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+KERNEL_SOURCES = ("gemm.hip", "rht.hip", "moe.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_diffusion_lm_tq4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(key: str):
+    """HBM bytes per launch from committed PMC counters, if they match the source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_loop(torch, fn, steps: int, warmup: int) -> float:
+    """Average ms per call of fn(i) over `steps` calls, HIP events on the stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(warmup + i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def bf16_dev(torch, np, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------- legs
+
+def dense_leg(torch, np, ops, I, wl, steps, warmup, copies, dev, sb):
+    """Returns dict with step time, kernel time and work figures for a dense workload."""
+    w = I.weights(wl.n, wl.k, wl.weights)
+    packed = ops.pack(torch.from_numpy(w).to(dev), sb)
+    del w
+    stack = [packed] + [packed.clone() for _ in range(copies - 1)]
+    x = bf16_dev(torch, np, I.activations_bf16(wl.m, wl.k), dev)
+    y = torch.empty((wl.m, wl.n), dtype=torch.float32, device=dev)
+    ws = torch.zeros(ops.linear_workspace_size(wl.m, wl.k, wl.n), dtype=torch.uint8, device=dev)
+    xt = ops.act_rht(x, sb)
+
+    def step(i):
+        ops.linear(x, stack[i % copies], sb, out=y, workspace=ws)
+
+    def kernel(i):
+        ops.linear_rotated(xt, stack[i % copies], out=y, workspace=ws)
+
+    ms_step = time_loop(torch, step, steps, warmup)
+    ms_kernel = time_loop(torch, kernel, steps, warmup)
+    packed_bytes = packed.numel()
+    flops = 2.0 * wl.m * wl.n * wl.k
+    return dict(ms_step=ms_step, ms_kernel=ms_kernel, packed_bytes=packed_bytes, flops=flops)
+
+
+def moe_setup(torch, np, ops, I, dev, sb, n1=1856, k=2688, n_exp=128):
+    from concurrent.futures import ThreadPoolExecutor
+    w1 = torch.empty((n_exp, n1, k // 32, 20), dtype=torch.uint8, device=dev)
+    w2 = torch.empty((n_exp, k, n1 // 32, 20), dtype=torch.uint8, device=dev)
+
+    def gen(e):
+        return e, I.expert_weights(e, 1, n1, k), I.expert_weights(e, 2, n1, k)
+
+    with ThreadPoolExecutor(8) as ex:
+        for lo in range(0, n_exp, 16):
+            for e, a, b in ex.map(gen, range(lo, min(lo + 16, n_exp))):
+                w1[e] = ops.pack(torch.from_numpy(a).to(dev), sb)
+                w2[e] = ops.pack(torch.from_numpy(b).to(dev), sb)
+    return w1, w2
+
+
+def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb):
+    ids, g = I.moe_routing(wl)
+    x = bf16_dev(torch, np, I.activations_bf16(wl.t, wl.k), dev)
+    idt = torch.from_numpy(ids).to(dev)
+    gt = torch.from_numpy(g).to(dev)
+    out = torch.empty((wl.t, wl.k), dtype=torch.float32, device=dev)
+    ws = torch.zeros(ops.moe_workspace_size(wl.t, wl.topk, wl.n_experts, wl.n1, wl.k),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        ops.moe_grouped(x, idt, gt, experts[0], experts[1], sb, out=out, workspace=ws)
+
+    ms = time_loop(torch, step, steps, warmup)
+    touched = np.unique(ids).size
+    per_expert = (wl.n1 * (wl.k // 32) + wl.k * (wl.n1 // 32)) * 20
+    pairs = wl.t * wl.topk
+    return dict(ms_step=ms, packed_bytes=touched * per_expert,
+                flops=2.0 * pairs * 2 * wl.n1 * wl.k, experts_touched=int(touched))
+
+
+# ----------------------------------------------------------------------- CPU side
+
+def cpu_baseline(np, I, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded slice of the M=16 workload, all host threads."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    rows = 1024
+    w = I.weights(rows, 2688)
+    sb = I.sign_bits()
+    packed = O.pack(w, sb)
+    x = I.activations_bf16(16, 2688)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        O.linear(x, packed, sb)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    gbs = packed.nbytes * calls / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"dense M=16 K=2688 projection, {rows} of 8192 weight rows "
+                      f"(unpack + rotate + fp64 matmul), {calls} calls in {el:.1f} s"}
+
+
+# ---------------------------------------------------------------------------- main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=48)
+    ap.add_argument("--legs", default="all",
+                    help="all | none | comma list of dense_m4096_t3,moe_t16,"
+                         "moe_t1024_uniform,moe_t1024_zipf")
+    ap.add_argument("--only", default=None,
+                    help="profile helper: run just this workload (no JSON contract)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="with --only: also run a plain 512 MiB device copy three times, "
+                         "the reference for scaling HBM byte counters")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from block_diffusion_lm_tq4_amd import inputs as I
+    from block_diffusion_lm_tq4_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    sb = I.sign_bits()
+
+    if args.only:
+        wl = I.WORKLOADS[args.only]
+        if args.only.startswith("dense"):
+            r = dense_leg(torch, np, ops, I, wl, args.steps, args.warmup, args.copies, dev, sb)
+        else:
+            ex = moe_setup(torch, np, ops, I, dev, sb)
+            r = moe_leg(torch, np, ops, I, wl, ex, args.steps, args.warmup, dev, sb)
+        log(args.only, json.dumps(r))
+        if args.copy_calibration:
+            src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log("copy calibration: 3 x 536870912 bytes read and written")
+        return 0
+
+    wl = I.WORKLOADS["dense_m16"]
+    log("dense_m16: packing weights")
+    r = dense_leg(torch, np, ops, I, wl, args.steps, args.warmup, args.copies, dev, sb)
+    gbs = r["packed_bytes"] / (r["ms_step"] * 1e-3) / 1e9
+    k_gbs = r["packed_bytes"] / (r["ms_kernel"] * 1e-3) / 1e9
+    log(f"dense_m16: step {r['ms_step'] * 1e3:.2f} us ({gbs:.0f} GB/s), "
+        f"dequant-GEMM kernel {r['ms_kernel'] * 1e3:.2f} us ({k_gbs:.0f} GB/s)")
+    roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic("dense_m16"),
+                "kernel": "gemm_kernel (tq4_linear_rotated), packed bytes per launch "
+                          f"{r['packed_bytes']}"}
+
+    legs = {}
+    names = ([] if args.legs == "none" else
+             ["dense_m4096_t3", "moe_t16", "moe_t1024_uniform", "moe_t1024_zipf"]
+             if args.legs == "all" else args.legs.split(","))
+    experts = None
+    for name in names:
+        wl2 = I.WORKLOADS[name]
+        if name.startswith("dense"):
+            log(f"{name}: running")
+            s2 = max(5, args.steps // 20)
+            q = dense_leg(torch, np, ops, I, wl2, s2, max(2, args.warmup // 10), 2, dev, sb)
+            tf = q["flops"] / (q["ms_step"] * 1e-3) / 1e12
+            ktf = q["flops"] / (q["ms_kernel"] * 1e-3) / 1e12
+            legs[name] = {"ms_per_step": round(q["ms_step"], 4), "TFLOP/s": round(tf, 1),
+                          "kernel_ms": round(q["ms_kernel"], 4),
+                          "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
+                                       "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(ktf / MFMA_F16_PEAK_TFLOPS, 4)}}
+        else:
+            if experts is None:
+                log("moe: generating and packing 128 experts")
+                experts = moe_setup(torch, np, ops, I, dev, sb)
+            log(f"{name}: running")
+            s2 = max(5, args.steps // 10)
+            q = moe_leg(torch, np, ops, I, wl2, experts, s2, max(2, args.warmup // 5), dev, sb)
+            g2 = q["packed_bytes"] / (q["ms_step"] * 1e-3) / 1e9
+            tf = q["flops"] / (q["ms_step"] * 1e-3) / 1e12
+            legs[name] = {"ms_per_step": round(q["ms_step"], 4), "GB/s": round(g2, 1),
+                          "TFLOP/s": round(tf, 2), "experts_touched": q["experts_touched"],
+                          "roofline": {"bound": "hbm", "achieved": round(g2, 1),
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": round(g2 / HBM_PEAK_GBS, 4)}}
+        log(name, json.dumps(legs[name]))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu_baseline: timing the fp64 oracle")
+        cpu = cpu_baseline(np, I)
+
+    line = {
+        "metric": "packed-weight GB/s & TFLOP/s of TQ4_1S dequant-GEMM at M=16 and M=4096",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "dense_m16: TQ4_1S linear, M=16 tokens, K=2688, N=8192, "
+                               "W~N(0,0.02^2) packed, x bf16~N(0,1), "
+                               f"{args.copies} rotating weight copies",
+                   "global_batch": wl.m, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -23,17 +23,23 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 int device_status(hipError_t e) { return e == hipSuccess ? TQ4_OK : TQ4_E_DEVICE; }
 
-// ---- tq4_linear workspace: [xt fp16 m*k][partials][counters] -------------
+// ---- tq4_linear workspace: [counters, fixed][xt fp16 m*k][partials] ------
+// The split-K tile counters always sit in the first kCounterBytes, whatever
+// the shapes, and every call leaves them at zero; split-K is only planned for
+// fewer than 256 output tiles, so 256 counters always suffice.
+constexpr size_t kCounterBytes = 1024;
+
 struct LinearLayout {
-  size_t xt, partial, counters, total;
+  size_t counters, xt, partial, total;
 };
 
 LinearLayout linear_layout(int64_t m, int64_t k, int64_t n, const DensePlan &p) {
+  (void)n;
   LinearLayout l{};
-  l.xt = 0;
-  l.partial = align_up(static_cast<size_t>(m) * k * 2);
-  l.counters = l.partial + align_up(p.partial_bytes);
-  l.total = l.counters + align_up(p.counter_bytes);
+  l.counters = 0;
+  l.xt = kCounterBytes;
+  l.partial = l.xt + align_up(static_cast<size_t>(m) * k * 2);
+  l.total = l.partial + align_up(p.partial_bytes);
   return l;
 }
 
@@ -145,11 +151,32 @@ int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *pack
   uint16_t *xt = reinterpret_cast<uint16_t *>(ws + l.xt);
   int32_t *counters = reinterpret_cast<int32_t *>(ws + l.counters);
   hipError_t e = tq4::launch_act_rht_bf16(x_bf16, m, k, sign_bits, xt, s, counters,
-                                          static_cast<int64_t>(p.counter_bytes / 4));
+                                          static_cast<int64_t>(kCounterBytes / 4));
   if (e != hipSuccess) return TQ4_E_DEVICE;
   e = tq4::launch_dense(p, xt, m, k, packed, n, y, reinterpret_cast<float *>(ws + l.partial),
                         counters, s);
   return device_status(e);
+}
+
+int tq4_linear_rotated(const uint16_t *xt_f16, int64_t m, int64_t k, const uint8_t *packed,
+                       int64_t n, float *y, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  if (m < 0 || k < 0 || n < 0 || k % 32 != 0) return TQ4_E_SHAPE;
+  if (m == 0 || n == 0) return TQ4_OK;
+  if (y == nullptr) return TQ4_E_NULL;
+  if (!aligned(y, 4)) return TQ4_E_ALIGN;
+  hipStream_t s = as_stream(stream);
+  if (k == 0) return device_status(tq4::launch_fill_zero(y, m * n, s));
+  if (xt_f16 == nullptr || packed == nullptr) return TQ4_E_NULL;
+  if (!aligned(xt_f16, 16) || !aligned(packed, 4)) return TQ4_E_ALIGN;
+  const DensePlan p = tq4::plan_dense(m, k, n);
+  const LinearLayout l = linear_layout(m, k, n, p);
+  if (workspace == nullptr || workspace_bytes < l.total) return TQ4_E_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
+  char *ws = static_cast<char *>(workspace);
+  return device_status(tq4::launch_dense(p, xt_f16, m, k, packed, n, y,
+                                         reinterpret_cast<float *>(ws + l.partial),
+                                         reinterpret_cast<int32_t *>(ws + l.counters), s));
 }
 
 int tq4_moe_route(const int32_t *topk_ids, int64_t t, int32_t topk, int32_t n_experts,

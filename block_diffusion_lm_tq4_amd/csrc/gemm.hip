@@ -338,6 +338,8 @@ DensePlan plan_dense(int64_t m, int64_t k, int64_t n) {
   const int64_t tiles = p.m_tiles * p.n_tiles;
   int64_t ks = 1;
   const int64_t target = 256;  // one workgroup per compute unit
+  // split-K only below 256 output tiles: the tile counters then fit in the
+  // fixed 256-entry counter area of the workspace
   if (tiles < target && p.chunks > 1) {
     ks = (target + tiles - 1) / tiles;
     if (ks > p.chunks) ks = p.chunks;

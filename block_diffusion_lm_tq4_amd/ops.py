@@ -35,7 +35,7 @@ def _cuda_contig(t: torch.Tensor, name: str, dtype) -> None:
 
 
 class Workspace:
-    """Grow-only device scratch buffers, one per (device, purpose)."""
+    """Grow-only, zero-initialised device scratch buffers, one per (device, purpose)."""
 
     def __init__(self):
         self._bufs: dict = {}
@@ -44,7 +44,7 @@ class Workspace:
         k = (str(device), key)
         buf = self._bufs.get(k)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            buf = torch.zeros(max(nbytes, 1024), dtype=torch.uint8, device=device)
             self._bufs[k] = buf
         return buf
 
@@ -111,6 +111,28 @@ def linear(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
                                          sign_bits & 0xFFFFFFFF, out.data_ptr(),
                                          workspace.data_ptr(), workspace.numel(),
                                          _stream(x.device)))
+    return out
+
+
+def linear_rotated(xt: torch.Tensor, packed: torch.Tensor, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = xt . Z_hat^T with xt = act_rht(x) already rotated (tq4_linear_rotated)."""
+    _cuda_contig(xt, "xt", torch.float16)
+    _cuda_contig(packed, "packed", torch.uint8)
+    m, k = xt.shape
+    _require(packed.dim() == 3 and packed.shape[1] * BLOCK == k and packed.shape[2] == BLOCK_BYTES,
+             "packed must be [n, k/32, 20]")
+    n = packed.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=xt.device)
+    _cuda_contig(out, "out", torch.float32)
+    _require(tuple(out.shape) == (m, n), "out must be [m, n]")
+    need = linear_workspace_size(m, k, n)
+    if workspace is None:
+        workspace = _WS.get(xt.device, "linear", need)
+    check("tq4_linear_rotated", lib().tq4_linear_rotated(
+        xt.data_ptr(), m, k, packed.data_ptr(), n, out.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream(xt.device)))
     return out
 
 

@@ -92,8 +92,10 @@ int tq4_pack(const float *w, int64_t n, int64_t k, uint32_t sign_bits,
 int tq4_act_rht(const uint16_t *x_bf16, int64_t m, int64_t k, uint32_t sign_bits,
                 uint16_t *xt_f16, void *stream);
 
-/* Workspace bytes tq4_linear needs for these sizes (0 if the sizes are
- * invalid).  No initial contents are required. */
+/* Workspace bytes tq4_linear and tq4_linear_rotated need for these sizes (0 if
+ * the sizes are invalid).  tq4_linear needs no initial contents;
+ * tq4_linear_rotated needs the first 1024 bytes zero before the workspace's
+ * first use (every call of either function leaves them zero again). */
 size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n);
 
 /* The on-the-fly dequantizing linear layer (model card, section Running it):
@@ -112,6 +114,17 @@ size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n);
 int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k,
                const uint8_t *packed, int64_t n, uint32_t sign_bits, float *y,
                void *workspace, size_t workspace_bytes, void *stream);
+
+/* The same product with the activations already rotated: y = xt . Z_hat^T,
+ * where xt = tq4_act_rht(x) (fp16 bit patterns [m, k], device, 16-byte
+ * aligned) and Z_hat[n, 32b + j] = S_h * c_q of the packed block (n, b).
+ * One rotation can then serve several projections of the same activations
+ * (model card, Running it: every quantized Linear of a layer reads the same
+ * input).  Same workspace, errors and determinism as tq4_linear; the first
+ * 1024 workspace bytes must be zero before the workspace's first use. */
+int tq4_linear_rotated(const uint16_t *xt_f16, int64_t m, int64_t k,
+                       const uint8_t *packed, int64_t n, float *y, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* Stable bucketing of the t*topk (token, slot) pairs by expert, the routing
  * step of the sync-free MoE (model card, Running it; 128 experts, top-6 in

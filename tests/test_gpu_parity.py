@@ -184,6 +184,16 @@ def test_linear_workspace_reuse_across_shapes(dev):
         _check_close(y, O.linear(x, O.pack(w, SB), SB), f"ws reuse {m}x{k}x{n}")
 
 
+@pytest.mark.parametrize("m,k,n", [(16, 2688, 8192), (7, 96, 40), (300, 256, 200)])
+def test_linear_rotated_equals_linear(dev, m, k, n):
+    w = I.weights(n, k, seed=3)
+    x = _bf16(I.activations_bf16(m, k), dev)
+    p = _ops().pack(torch.from_numpy(w).to(dev), SB)
+    a = _ops().linear(x, p, SB)
+    b = _ops().linear_rotated(_ops().act_rht(x, SB), p)
+    assert torch.equal(a, b)
+
+
 def test_linear_k0_writes_zeros(dev):
     x = torch.empty((4, 0), dtype=torch.bfloat16, device=dev)
     p = torch.empty((8, 0, 20), dtype=torch.uint8, device=dev)
