@@ -29,6 +29,7 @@ SOURCES = {
     "pack.hip": ["-ffp-contract=off"],
     "rht.hip": [],
     "gemm.hip": [],
+    "skinny.hip": [],
     "moe.hip": [],
 }
 

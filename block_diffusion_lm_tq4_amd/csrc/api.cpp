@@ -23,24 +23,28 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 int device_status(hipError_t e) { return e == hipSuccess ? TQ4_OK : TQ4_E_DEVICE; }
 
-// ---- tq4_linear workspace: [counters, fixed][xt fp16 m*k][partials] ------
-// The split-K tile counters always sit in the first kCounterBytes, whatever
-// the shapes, and every call leaves them at zero; split-K is only planned for
-// fewer than 256 output tiles, so 256 counters always suffice.
-constexpr size_t kCounterBytes = 1024;
-
+// ---- tq4_linear workspace ------------------------------------------------
+// m <= 16: one fused kernel, no workspace.  Otherwise [xt fp16 m*k][split-K
+// partial sums].  tq4_linear_rotated needs only the partial sums.
 struct LinearLayout {
-  size_t counters, xt, partial, total;
+  size_t xt, partial, total;
 };
 
-LinearLayout linear_layout(int64_t m, int64_t k, int64_t n, const DensePlan &p) {
-  (void)n;
+LinearLayout linear_layout(int64_t m, int64_t k, int64_t n, bool rotated) {
   LinearLayout l{};
-  l.counters = 0;
-  l.xt = kCounterBytes;
-  l.partial = l.xt + align_up(static_cast<size_t>(m) * k * 2);
+  if (!rotated && tq4::skinny_fits(m, k)) return l;
+  const DensePlan p = tq4::plan_dense(m, k, n);
+  l.xt = 0;
+  l.partial = rotated ? 0 : align_up(static_cast<size_t>(m) * k * 2);
   l.total = l.partial + align_up(p.partial_bytes);
   return l;
+}
+
+int check_workspace(const void *ws, size_t bytes, size_t need) {
+  if (need == 0) return TQ4_OK;
+  if (ws == nullptr || bytes < need) return TQ4_E_WORKSPACE;
+  if (!aligned(ws, kAlign)) return TQ4_E_ALIGN;
+  return TQ4_OK;
 }
 
 // ---- tq4_moe_grouped workspace ------------------------------------------
@@ -128,8 +132,9 @@ int tq4_act_rht(const uint16_t *x_bf16, int64_t m, int64_t k, uint32_t sign_bits
 
 size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n) {
   if (m < 0 || k < 0 || n < 0 || k % 32 != 0) return 0;
-  const DensePlan p = tq4::plan_dense(m, k, n);
-  return linear_layout(m, k, n, p).total;
+  const size_t a = linear_layout(m, k, n, false).total;
+  const size_t b = linear_layout(m, k, n, true).total;
+  return a > b ? a : b;
 }
 
 int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed, int64_t n,
@@ -143,18 +148,17 @@ int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *pack
   if (k == 0) return device_status(tq4::launch_fill_zero(y, m * n, s));
   if (x_bf16 == nullptr || packed == nullptr) return TQ4_E_NULL;
   if (!aligned(x_bf16, 16) || !aligned(packed, 4)) return TQ4_E_ALIGN;
-  const DensePlan p = tq4::plan_dense(m, k, n);
-  const LinearLayout l = linear_layout(m, k, n, p);
-  if (workspace == nullptr || workspace_bytes < l.total) return TQ4_E_WORKSPACE;
-  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
+  const LinearLayout l = linear_layout(m, k, n, false);
+  const int ws_status = check_workspace(workspace, workspace_bytes, l.total);
+  if (ws_status != TQ4_OK) return ws_status;
+  if (tq4::skinny_fits(m, k))
+    return device_status(tq4::launch_skinny(x_bf16, m, k, packed, n, sign_bits, y, s));
   char *ws = static_cast<char *>(workspace);
   uint16_t *xt = reinterpret_cast<uint16_t *>(ws + l.xt);
-  int32_t *counters = reinterpret_cast<int32_t *>(ws + l.counters);
-  hipError_t e = tq4::launch_act_rht_bf16(x_bf16, m, k, sign_bits, xt, s, counters,
-                                          static_cast<int64_t>(kCounterBytes / 4));
+  hipError_t e = tq4::launch_act_rht_bf16(x_bf16, m, k, sign_bits, xt, s);
   if (e != hipSuccess) return TQ4_E_DEVICE;
-  e = tq4::launch_dense(p, xt, m, k, packed, n, y, reinterpret_cast<float *>(ws + l.partial),
-                        counters, s);
+  const DensePlan p = tq4::plan_dense(m, k, n);
+  e = tq4::launch_dense(p, xt, m, k, packed, n, y, reinterpret_cast<float *>(ws + l.partial), s);
   return device_status(e);
 }
 
@@ -169,14 +173,13 @@ int tq4_linear_rotated(const uint16_t *xt_f16, int64_t m, int64_t k, const uint8
   if (k == 0) return device_status(tq4::launch_fill_zero(y, m * n, s));
   if (xt_f16 == nullptr || packed == nullptr) return TQ4_E_NULL;
   if (!aligned(xt_f16, 16) || !aligned(packed, 4)) return TQ4_E_ALIGN;
+  const LinearLayout l = linear_layout(m, k, n, true);
+  const int ws_status = check_workspace(workspace, workspace_bytes, l.total);
+  if (ws_status != TQ4_OK) return ws_status;
   const DensePlan p = tq4::plan_dense(m, k, n);
-  const LinearLayout l = linear_layout(m, k, n, p);
-  if (workspace == nullptr || workspace_bytes < l.total) return TQ4_E_WORKSPACE;
-  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
   char *ws = static_cast<char *>(workspace);
   return device_status(tq4::launch_dense(p, xt_f16, m, k, packed, n, y,
-                                         reinterpret_cast<float *>(ws + l.partial),
-                                         reinterpret_cast<int32_t *>(ws + l.counters), s));
+                                         reinterpret_cast<float *>(ws + l.partial), s));
 }
 
 int tq4_moe_route(const int32_t *topk_ids, int64_t t, int32_t topk, int32_t n_experts,

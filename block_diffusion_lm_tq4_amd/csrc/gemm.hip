@@ -23,11 +23,10 @@
 // word t for step t, scales word 4) and 64 contiguous bytes of xt per
 // activation tile.
 //
-// Split-K.  For skinny shapes the K axis is cut into `ksplit` ranges; each
-// workgroup writes its fp32 partial tile, and the last workgroup to finish a
-// tile (found with a device-scope counter) adds the partials in split order,
-// writes y and re-arms the counter.  The result does not depend on which
-// workgroup finishes last.
+// Split-K.  When there are too few output tiles to fill the chip, the K axis
+// is cut into `ksplit` ranges; each workgroup writes an fp32 partial tile and
+// a second kernel adds the partials in split order (deterministic, and the
+// kernel boundary is the only synchronization needed).
 //
 // MoE.  The same core runs over a device-built list of (expert, first row,
 // rows) tiles.  Mode up gathers activation rows through the bucket
@@ -50,7 +49,6 @@ struct GemmArgs {
   const uint8_t *w;          // packed weights [n][k/32][20] (per expert for MoE)
   float *out;                // output rows, stride n
   float *partial;            // [ksplit][m][n] (dense split-K)
-  int32_t *counters;         // one per output tile (dense split-K)
   const int32_t *perm;       // MoE: bucket position -> pair
   const MoETile *tiles;      // MoE tile list
   const int32_t *n_tiles;    // MoE tile count (device)
@@ -99,7 +97,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
   constexpr int WG_N = 16 * NSUB * WN;
 
   __shared__ uint32_t lut[256];
-  __shared__ int32_t s_last;
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
@@ -249,28 +246,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
           if (m < g.m && n < g.n) dst[m * g.n + n] = acc[i][j][v];
         }
       }
-    if (g.ksplit > 1) {
-      __threadfence();
-      __syncthreads();
-      const int64_t tile = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
-      if (tid == 0) s_last = (atomicAdd(&g.counters[tile], 1) == g.ksplit - 1);
-      __syncthreads();
-      if (s_last) {
-        __threadfence();
-        const int64_t mn = g.m * g.n;
-        for (int e = tid; e < WG_M * WG_N; e += 64 * WM * WN) {
-          const int64_t m = m_base + e / WG_N;
-          const int64_t n = n_base + e % WG_N;
-          if (m < g.m && n < g.n) {
-            const float *p = g.partial + m * g.n + n;
-            float s = p[0];
-            for (int q = 1; q < g.ksplit; ++q) s += p[q * mn];
-            g.out[m * g.n + n] = s;
-          }
-        }
-        if (tid == 0) g.counters[tile] = 0;
-      }
-    }
   } else {
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
@@ -290,6 +265,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
         }
       }
   }
+}
+
+// y[i] = sum over splits of partial[s][i], in split order.
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ partial,
+                                                              int32_t ksplit, int64_t mn,
+                                                              float *__restrict__ y) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= mn) return;
+  float s = partial[i];
+  for (int q = 1; q < ksplit; ++q) s += partial[q * mn + i];
+  y[i] = s;
 }
 
 template <int MSUB, int NSUB, int WM, int WN, int MODE>
@@ -338,8 +324,6 @@ DensePlan plan_dense(int64_t m, int64_t k, int64_t n) {
   const int64_t tiles = p.m_tiles * p.n_tiles;
   int64_t ks = 1;
   const int64_t target = 256;  // one workgroup per compute unit
-  // split-K only below 256 output tiles: the tile counters then fit in the
-  // fixed 256-entry counter area of the workspace
   if (tiles < target && p.chunks > 1) {
     ks = (target + tiles - 1) / tiles;
     if (ks > p.chunks) ks = p.chunks;
@@ -347,19 +331,17 @@ DensePlan plan_dense(int64_t m, int64_t k, int64_t n) {
   }
   p.ksplit = static_cast<int>(ks);
   p.partial_bytes = ks > 1 ? static_cast<size_t>(ks) * m * n * sizeof(float) : 0;
-  p.counter_bytes = ks > 1 ? static_cast<size_t>(tiles) * sizeof(int32_t) : 0;
   return p;
 }
 
 hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64_t k,
                         const uint8_t *packed, int64_t n, float *y, float *partial,
-                        int32_t *counters, hipStream_t s) {
+                        hipStream_t s) {
   GemmArgs g{};
   g.a = xt;
   g.w = packed;
   g.out = y;
   g.partial = partial;
-  g.counters = counters;
   g.m = m;
   g.n = n;
   g.k = k;
@@ -368,7 +350,12 @@ hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64
   g.cb = codebook();
   const dim3 grid(static_cast<unsigned>(p.n_tiles), static_cast<unsigned>(p.m_tiles),
                   static_cast<unsigned>(p.ksplit));
-  return dispatch<kDense>(p.msub, p.nsub, p.waves_m, p.waves_n, g, grid, s);
+  hipError_t e = dispatch<kDense>(p.msub, p.nsub, p.waves_m, p.waves_n, g, grid, s);
+  if (e != hipSuccess || p.ksplit == 1) return e;
+  const int64_t mn = m * n;
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3(static_cast<unsigned>((mn + 255) / 256)),
+                     dim3(256), 0, s, partial, p.ksplit, mn, y);
+  return hipGetLastError();
 }
 
 MoEPlan plan_moe(int64_t pairs, int32_t n_experts) {

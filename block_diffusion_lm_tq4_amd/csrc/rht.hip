@@ -42,18 +42,11 @@ __device__ inline void load_block<float>(const float *p, float (&v)[32]) {
   }
 }
 
-// Besides the rotation, the kernel clears `zero_count` int32 words at `zero`
-// (the split-K tile counters of the product that follows on the stream), so
-// that product never depends on what an earlier call left in the workspace.
 template <typename In>
 __global__ __launch_bounds__(256) void act_rht_kernel(const In *__restrict__ x, int64_t n_blocks,
                                                       uint32_t sign_bits,
-                                                      uint16_t *__restrict__ xt,
-                                                      int32_t *__restrict__ zero,
-                                                      int64_t zero_count) {
+                                                      uint16_t *__restrict__ xt) {
   const int64_t blk = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (int64_t i = blk; i < zero_count; i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    zero[i] = 0;
   if (blk >= n_blocks) return;
   float v[32];
   load_block<In>(x + blk * 32, v);
@@ -89,13 +82,13 @@ __global__ __launch_bounds__(256) void act_rht_kernel(const In *__restrict__ x, 
 
 template <typename In>
 hipError_t launch(const In *x, int64_t m, int64_t k, uint32_t sign_bits, uint16_t *xt,
-                  hipStream_t s, int32_t *zero, int64_t zero_count) {
+                  hipStream_t s) {
   const int64_t n_blocks = m * (k / 32);
   if (n_blocks == 0) return hipSuccess;
   const int threads = 256;
   const int64_t grid = (n_blocks + threads - 1) / threads;
   hipLaunchKernelGGL(act_rht_kernel<In>, dim3(static_cast<unsigned>(grid)), dim3(threads), 0, s,
-                     x, n_blocks, sign_bits, xt, zero, zero_count);
+                     x, n_blocks, sign_bits, xt);
   return hipGetLastError();
 }
 
@@ -114,13 +107,13 @@ hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s) {
 }
 
 hipError_t launch_act_rht_bf16(const uint16_t *x, int64_t m, int64_t k, uint32_t sign_bits,
-                               uint16_t *xt, hipStream_t s, int32_t *zero, int64_t zero_count) {
-  return launch<uint16_t>(x, m, k, sign_bits, xt, s, zero, zero_count);
+                               uint16_t *xt, hipStream_t s) {
+  return launch<uint16_t>(x, m, k, sign_bits, xt, s);
 }
 
 hipError_t launch_act_rht_f32(const float *x, int64_t m, int64_t k, uint32_t sign_bits,
                               uint16_t *xt, hipStream_t s) {
-  return launch<float>(x, m, k, sign_bits, xt, s, nullptr, 0);
+  return launch<float>(x, m, k, sign_bits, xt, s);
 }
 
 }  // namespace tq4

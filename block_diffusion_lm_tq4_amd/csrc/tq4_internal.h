@@ -18,11 +18,9 @@ const Codebook &codebook();
 hipError_t launch_pack(const float *w, int64_t n_blocks, uint32_t sign_bits,
                        uint8_t *packed, int32_t *nonfinite, hipStream_t s);
 
-// Rotate [m, k] rows (bf16 or fp32) to fp16; the bf16 variant also clears
-// `zero_count` int32 words at `zero`.
+// Rotate [m, k] rows (bf16 or fp32) to fp16.
 hipError_t launch_act_rht_bf16(const uint16_t *x, int64_t m, int64_t k, uint32_t sign_bits,
-                               uint16_t *xt, hipStream_t s, int32_t *zero = nullptr,
-                               int64_t zero_count = 0);
+                               uint16_t *xt, hipStream_t s);
 hipError_t launch_act_rht_f32(const float *x, int64_t m, int64_t k, uint32_t sign_bits,
                               uint16_t *xt, hipStream_t s);
 
@@ -36,12 +34,17 @@ struct DensePlan {
   int waves_n;    // waves per workgroup along n
   int ksplit;     // workgroups along k (partial sums reduced in fixed order)
   int64_t m_tiles, n_tiles, chunks;
-  size_t partial_bytes, counter_bytes;  // workspace needs beyond xt
+  size_t partial_bytes;  // split-K partial sums (workspace, beyond xt)
 };
 DensePlan plan_dense(int64_t m, int64_t k, int64_t n);
 hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64_t k,
                         const uint8_t *packed, int64_t n, float *y, float *partial,
-                        int32_t *counters, hipStream_t s);
+                        hipStream_t s);
+
+// Single-kernel path for m <= 16 (rotation fused, no workspace).
+bool skinny_fits(int64_t m, int64_t k);
+hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
+                         int64_t n, uint32_t sign_bits, float *y, hipStream_t s);
 
 // MoE pieces.
 struct MoETile {  // one m-tile of one expert's segment in bucket order

@@ -92,10 +92,9 @@ int tq4_pack(const float *w, int64_t n, int64_t k, uint32_t sign_bits,
 int tq4_act_rht(const uint16_t *x_bf16, int64_t m, int64_t k, uint32_t sign_bits,
                 uint16_t *xt_f16, void *stream);
 
-/* Workspace bytes tq4_linear and tq4_linear_rotated need for these sizes (0 if
- * the sizes are invalid).  tq4_linear needs no initial contents;
- * tq4_linear_rotated needs the first 1024 bytes zero before the workspace's
- * first use (every call of either function leaves them zero again). */
+/* Workspace bytes that suffice for both tq4_linear and tq4_linear_rotated at
+ * these sizes (0 if the sizes are invalid, or if neither needs scratch, e.g.
+ * m <= 16).  No initial contents are required. */
 size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n);
 
 /* The on-the-fly dequantizing linear layer (model card, section Running it):
@@ -106,8 +105,10 @@ size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n);
  *   y       : [m, n] fp32, device, 4-byte aligned, overwritten
  *   workspace / workspace_bytes : device scratch of at least
  *             tq4_linear_workspace_size(m, k, n) bytes, 256-byte aligned
- * The rotation is applied to the activations (tq4_act_rht) and the product
- * runs on 16-bit MFMA with fp32 accumulation; results are deterministic.
+ *             (may be NULL when that size is 0)
+ * The rotation is applied to the activations (R x, see tq4_act_rht) and the
+ * product runs on 16-bit MFMA with fp32 accumulation; results are
+ * deterministic.  For m <= 16 and k <= 4096 this is a single kernel.
  * Errors: TQ4_E_NULL, TQ4_E_SHAPE (negative sizes, k % 32 != 0),
  * TQ4_E_ALIGN, TQ4_E_WORKSPACE, TQ4_E_DEVICE.  m == 0 or n == 0 is a no-op;
  * k == 0 writes zeros. */
@@ -120,8 +121,7 @@ int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k,
  * aligned) and Z_hat[n, 32b + j] = S_h * c_q of the packed block (n, b).
  * One rotation can then serve several projections of the same activations
  * (model card, Running it: every quantized Linear of a layer reads the same
- * input).  Same workspace, errors and determinism as tq4_linear; the first
- * 1024 workspace bytes must be zero before the workspace's first use. */
+ * input).  Same workspace, errors and determinism as tq4_linear. */
 int tq4_linear_rotated(const uint16_t *xt_f16, int64_t m, int64_t k,
                        const uint8_t *packed, int64_t n, float *y, void *workspace,
                        size_t workspace_bytes, void *stream);

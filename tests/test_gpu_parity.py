@@ -313,3 +313,47 @@ def test_moe_small_shapes_and_invalid_ids(dev):
                                  torch.from_numpy(g).to(dev), torch.from_numpy(p1).to(dev),
                                  torch.from_numpy(p2).to(dev), SB).cpu().numpy()
         _check_close(out, O.moe(x, ids, g, list(p1), list(p2), SB), f"moe t{t} e{e}")
+
+
+# ------------------------------------------------------------------- graph replay
+
+def test_graph_replays_match_eager(dev, experts):
+    """Captured calls replayed several times, with eager work and syncs in
+    between, give the eager results bit for bit."""
+    ops = _ops()
+    w = I.weights(8192, 2688)
+    p = ops.pack(torch.from_numpy(w).to(dev), SB)
+    x16 = _bf16(I.activations_bf16(16, 2688), dev)
+    x100 = _bf16(I.activations_bf16(100, 2688), dev)
+    wl = I.WORKLOADS["moe_t16"]
+    ids, g = I.moe_routing(wl)
+    xm = _bf16(I.activations_bf16(wl.t, wl.k), dev)
+    idt, gt = torch.from_numpy(ids).to(dev), torch.from_numpy(g).to(dev)
+    y16 = torch.empty((16, 8192), device=dev)
+    y100 = torch.empty((100, 8192), device=dev)
+    om = torch.empty((wl.t, wl.k), device=dev)
+    ws_lin = torch.zeros(ops.linear_workspace_size(100, 2688, 8192), dtype=torch.uint8, device=dev)
+    ws_moe = torch.zeros(ops.moe_workspace_size(wl.t, 6, 128, 1856, 2688), dtype=torch.uint8,
+                         device=dev)
+
+    def run():
+        ops.linear(x16, p, SB, out=y16)
+        ops.linear(x100, p, SB, out=y100, workspace=ws_lin)
+        ops.moe_grouped(xm, idt, gt, experts[0], experts[1], SB, out=om, workspace=ws_moe)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [y16.clone(), y100.clone(), om.clone()]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for t in (y16, y100, om):
+            t.fill_(float("nan"))
+        junk = ops.linear(x100, p, SB)          # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk).all()
+        for a, b in zip((y16, y100, om), ref):
+            assert torch.equal(a, b), rep
