@@ -82,10 +82,10 @@ def test_act_rht_argument_errors(L):
 
 
 def test_linear_argument_errors(L):
-    ws = L.tq4_linear_workspace_size(16, 2688, 8192)
-    assert ws > 16 * 2688 * 2
+    ws = L.tq4_linear_workspace_size(100, 2688, 8192)
+    assert ws >= 100 * 2688 * 2                      # room for the rotated activations
     assert L.tq4_linear_workspace_size(16, 33, 8) == 0
-    args = dict(x=FAKE, m=16, k=2688, p=FAKE, n=8192, sb=0, y=FAKE, ws=FAKE, wsb=ws)
+    args = dict(x=FAKE, m=100, k=2688, p=FAKE, n=8192, sb=0, y=FAKE, ws=FAKE, wsb=ws)
 
     def call(**kw):
         a = dict(args, **kw)
