@@ -25,14 +25,14 @@ int device_status(hipError_t e) { return e == hipSuccess ? TQ4_OK : TQ4_E_DEVICE
 
 // ---- tq4_linear workspace ------------------------------------------------
 // m <= 16: one fused kernel, no workspace.  Otherwise [xt fp16 m*k][split-K
-// partial sums].  tq4_linear_rotated needs only the partial sums.
+// partial sums]; tq4_linear_rotated needs only the partial sums.
 struct LinearLayout {
   size_t xt, partial, total;
 };
 
 LinearLayout linear_layout(int64_t m, int64_t k, int64_t n, bool rotated) {
   LinearLayout l{};
-  if (!rotated && tq4::skinny_fits(m, k)) return l;
+  if (!rotated && tq4::skinny_fits(m, k, n)) return l;
   const DensePlan p = tq4::plan_dense(m, k, n);
   l.xt = 0;
   l.partial = rotated ? 0 : align_up(static_cast<size_t>(m) * k * 2);
@@ -132,6 +132,7 @@ int tq4_act_rht(const uint16_t *x_bf16, int64_t m, int64_t k, uint32_t sign_bits
 
 size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n) {
   if (m < 0 || k < 0 || n < 0 || k % 32 != 0) return 0;
+  if (m == 0 || n == 0 || k == 0) return 0;
   const size_t a = linear_layout(m, k, n, false).total;
   const size_t b = linear_layout(m, k, n, true).total;
   return a > b ? a : b;
@@ -151,7 +152,7 @@ int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *pack
   const LinearLayout l = linear_layout(m, k, n, false);
   const int ws_status = check_workspace(workspace, workspace_bytes, l.total);
   if (ws_status != TQ4_OK) return ws_status;
-  if (tq4::skinny_fits(m, k))
+  if (tq4::skinny_fits(m, k, n))
     return device_status(tq4::launch_skinny(x_bf16, m, k, packed, n, sign_bits, y, s));
   char *ws = static_cast<char *>(workspace);
   uint16_t *xt = reinterpret_cast<uint16_t *>(ws + l.xt);

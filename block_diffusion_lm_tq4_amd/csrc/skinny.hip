@@ -1,28 +1,43 @@
 // Decode-shaped TQ4_1S linear layer: up to 16 activation rows (one 16-token
 // diffusion block, the shape every denoiser projection sees on each step;
 // Nemotron-TheHobbit-30B-A3B model card, sections Running it and Performance
-// & why it's slow) in a single kernel launch.
+// & why it's slow) in a single kernel launch, rotation included.
 //
-// The weight stream is the whole cost here, so the kernel is built around it:
+// The weight stream is the whole cost, so the kernel is arranged to start
+// consuming weights as early as possible and to keep everything else off that
+// path.  A workgroup owns 32 weight rows (two 16-row MFMA tiles) and all of
+// K, with two kinds of waves:
 //
-//  1. Each lane issues the loads of all its 20-byte weight blocks at once
-//     (they stay in registers), before anything else, so the whole weight
-//     tile of the workgroup is in flight from HBM while the rest happens.
-//  2. The activations are rotated in the meantime, straight into LDS:
-//     xt_b = H32 diag(s) x_b / sqrt(32) is itself a product with a +-1 matrix,
-//     so two v_mfma_f32_16x16x32_bf16 per 32-block compute it exactly from the
-//     bf16 input (products by +-1 are exact, sums are fp32), and the fp32
-//     result is scaled and rounded to fp16.
-//  3. The decode + MFMA loop then reads activation fragments from LDS and
-//     decodes weights from registers (see gemm.hip for the operand mapping).
+//  * 4 producer waves bring x (16 rows of 2k bytes) into LDS with whole-row
+//    LDS-direct loads (1 KB per load instruction, every cache line fully
+//    used) and build the codebook pair table.  Their loads are issued before any weight load
+//    (a workgroup barrier orders the two), so x arrives first.
+//  * 8 consumer waves split K by chunks of 4 blocks (128 inputs).  Each
+//    issues every weight load it will need at once (its 20-byte block of each
+//    row tile, chunk by chunk) and then consumes the chunks in issue order: a
+//    wave's vector-memory counter retires in that order, so chunk i is used
+//    as soon as its own blocks are in while later chunks still stream.  (The
+//    two roles live in different waves for the same reason: a wave that both
+//    streamed weights and waited for x would wait for its weights too.)
 //
-// Workgroup = 8 waves over 32 weight rows.  Waves 0-3 hold the weights: wave
-// w takes rows (w & 1) * 16 .. +15 and the K half (w >> 1).  Waves 4-7 build
-// the codebook table and the rotated activations.  The split matters because
-// a wave's vector-memory counter retires in issue order: a wave that waited
-// for an activation load would also wait for every weight load it issued
-// before it.  The two K halves are added through LDS in a fixed order, so
-// results are deterministic and no workgroup ever waits on another one.
+// Per chunk, a consumer
+//  1. rotates the chunk's 4 activation blocks from LDS:
+//     xt_b = H32 diag(s) x_b / sqrt(32) is a product with a +-1 matrix, so two
+//     v_mfma_f32_16x16x32_bf16 per block compute it from the bf16 input
+//     (products by +-1 are exact, sums are fp32).  The MFMA rows are permuted
+//     so that lane group g receives xt elements 8g..8g+7 of the block: that is
+//     directly the activation operand of the block's product MFMA.  The
+//     1/sqrt(32) is applied once to y;
+//  2. transposes its weight words across the 4 lane groups (lane group g
+//     loaded block 4c+g; after two v_permlane32_swap and two
+//     v_permlane16_swap per 4 words it holds word g of every block), so that
+//     the product of block 4c+t takes elements 8g..8g+7 from lane group g;
+//  3. decodes in registers (four byte-indexed lookups of fp16 level pairs in
+//     an LDS table, one copy per lane % 8 to spread random lookups over the
+//     banks; one packed fp16 multiply by the half-block scale per pair) and
+//     accumulates with v_mfma_f32_16x16x32_f16.
+// The consumers' partial sums are added at the end in wave order, so results
+// are deterministic.
 #include "tq4_internal.h"
 
 namespace tq4 {
@@ -32,18 +47,23 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kRowsPerWG = 32;
-constexpr size_t kSkinnyMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
-constexpr int kLutBytes = 1024;
-constexpr int kRedBytes = 2 * 64 * 16;  // two waves' accumulators
+constexpr int kConsumers = 8;
+constexpr int kProducers = 4;
+constexpr int kThreads = 64 * (kConsumers + kProducers);
+constexpr int kRowTiles = 2;                 // 16-row MFMA tiles per workgroup
+constexpr int kRowsPerWG = 16 * kRowTiles;   // 32
+constexpr int kLutCopies = 8;
+constexpr int kMaxK = 4096;
+constexpr int kXStrideMax = kMaxK + 8;  // halves per x row slot in LDS
 
 struct SkinnyArgs {
-  const uint16_t *x;      // bf16 [m][k]
-  const uint8_t *w;       // packed [n][k/32][20]
-  float *y;               // [m][n]
-  int64_t m, n, k;
-  int32_t xt_stride;      // LDS row stride of the rotated activations, halves
+  const uint16_t *x;  // bf16 [m][k]
+  const uint8_t *w;   // packed [n][k/32][20]
+  float *y;           // [m][n]
+  int32_t m, n, kb;   // kb = k / 32
   uint32_t sign_bits;
   Codebook cb;
 };
@@ -52,11 +72,16 @@ __device__ inline uint32_t f16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(f)));
 }
 
+__device__ inline uint32_t pack_f16x2(float lo, float hi) {
+  return f16_bits(lo) | (f16_bits(hi) << 16);
+}
+
+// `lut` points at this lane's copy: entry e is lut[e * kLutCopies].
 __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *lut) {
-  const half2v p0 = __builtin_bit_cast(half2v, lut[codes & 0xFFu]) * scale;
-  const half2v p1 = __builtin_bit_cast(half2v, lut[(codes >> 8) & 0xFFu]) * scale;
-  const half2v p2 = __builtin_bit_cast(half2v, lut[(codes >> 16) & 0xFFu]) * scale;
-  const half2v p3 = __builtin_bit_cast(half2v, lut[codes >> 24]) * scale;
+  const half2v p0 = __builtin_bit_cast(half2v, lut[(codes & 0xFFu) * kLutCopies]) * scale;
+  const half2v p1 = __builtin_bit_cast(half2v, lut[((codes >> 8) & 0xFFu) * kLutCopies]) * scale;
+  const half2v p2 = __builtin_bit_cast(half2v, lut[((codes >> 16) & 0xFFu) * kLutCopies]) * scale;
+  const half2v p3 = __builtin_bit_cast(half2v, lut[(codes >> 24) * kLutCopies]) * scale;
   half8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
@@ -71,163 +96,218 @@ __device__ inline half2v scale_pair(uint32_t bf16_bits) {
   return r;
 }
 
-struct WRaw {
-  uint32_t v[5];
-};
+// 4x4 transpose across the lane groups (rows of 16 lanes): on entry lane
+// group g holds d[q] = D[g][q]; on exit it holds d[q] = D[q][g].
+__device__ inline void transpose4(uint32_t (&d)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  d[0] = c[0];
+  d[1] = c[1];
+  d[2] = e[0];
+  d[3] = e[1];
+}
 
-template <int CH>
-__global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs g) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t *lut = reinterpret_cast<uint32_t *>(smem);
-  floatx4 *red = reinterpret_cast<floatx4 *>(smem + kLutBytes);
-  _Float16 *xts = reinterpret_cast<_Float16 *>(smem + kLutBytes + kRedBytes);
+// CH >= chunks per consumer wave; XL >= ceil(k / 512) (loads per lane per x row).
+template <int CH, int XL>
+__global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
+  __shared__ uint32_t lut[256 * kLutCopies];
+  __shared__ floatx4 red[kConsumers][kRowTiles][64];  // consumers' partial sums
+  __shared__ uint16_t xs[16 * kXStrideMax];           // x rows
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
   const int r = lane % 16;
   const int grp = lane / 16;
-  const int64_t kb = g.k / 32;
+  const int kb = g.kb;
+  const int k = 32 * kb;
+  // x row slot in LDS: k rounded up to whole KB, plus 8 halves, so that
+  // consecutive rows start 4 banks apart (16-lane 16-byte reads of 16
+  // different rows then hit 64 distinct banks)
+  const int xstride = ((k + 511) / 512) * 512 + 8;
 
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  WRaw wr[CH];
-  uint32_t ok_mask = 0;  // bit i: chunk c0 + i holds a real block for this lane
-  int c0 = 0, c1 = 0;
-  int64_t n = 0;
-  bool n_ok = false;
-  const int rg = wave & 1;        // consumer: 16-row group
-  const int kh = (wave >> 1) & 1; // consumer: K half
-
-  if (wave < 4) {
-    // consumers: put this lane's whole weight share in flight first.  The
-    // loads are unconditional (a lane with no block here re-reads block 0 of
-    // row 0 and later zeroes its scales), so the compiler can retire them one
-    // chunk at a time instead of waiting for all of them before the first use.
-    const int chunks = static_cast<int>((kb + 3) / 4);
-    const int half = (chunks + 1) / 2;
-    c0 = kh ? half : 0;
-    c1 = kh ? chunks : half;
-    n = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + rg * 16 + r;
-    n_ok = n < g.n;
+  if (wave >= kConsumers) {
+    // ---------------------------------------------------------- producers
+    const int pw = wave - kConsumers;
+    const int ptid = tid - 64 * kConsumers;
+    // rows pw, pw + 4, pw + 8, pw + 12, loaded straight into LDS (16 bytes
+    // per lane, 1 KB per instruction).  Rows past m load row 0 (finite
+    // values; their outputs are never stored); lanes past the row end re-read
+    // piece 0 and land in the row's slack (the row slot is a whole number of
+    // KB plus 16 bytes).
+    const int row_pieces = k / 8;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = c0 + i;
-      const int64_t b = 4 * static_cast<int64_t>(c) + grp;
-      const bool ok = c < c1 && b < kb && n_ok;
-      ok_mask |= static_cast<uint32_t>(ok) << i;
-      const uint32_t *p = reinterpret_cast<const uint32_t *>(g.w + (ok ? (n * kb + b) * 20 : 0));
+    for (int h = 0; h < 4; ++h) {
+      const int rr = pw + 4 * h;
+      const uint16_t *src = g.x + (rr < g.m ? rr : 0) * k;
+      uint16_t *dst = xs + rr * xstride;
 #pragma unroll
-      for (int q = 0; q < 5; ++q) wr[i].v[q] = p[q];
-    }
-  } else {
-    // producers: codebook pair table, then the rotated activations in LDS.
-    const int ptid = tid - 256;
-    const int pw = wave - 4;
-    lut[ptid] = f16_bits(g.cb.c[ptid & 15]) | (f16_bits(g.cb.c[ptid >> 4]) << 16);
-    // MFMA rows are output elements j of the block, columns are activation
-    // rows m:  C[j][m] = sum_k H[j][k] s_k x[m][k].  Lane (r, grp) supplies
-    // H[j = r (+16)][8 grp + i] s_{8 grp + i} and x[m = r][8 grp + i]; it
-    // receives C[4 grp + v][r] = xt[r][4 grp + v (+16)].
-    bf16x8 h_lo, h_hi;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = 8 * grp + i;
-      const bool neg = ((__builtin_popcount(r & k) & 1) != 0) ^ (((g.sign_bits >> k) & 1u) != 0);
-      const uint16_t one = neg ? 0xBF80u : 0x3F80u;
-      h_lo[i] = __builtin_bit_cast(__bf16, one);
-      h_hi[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(k >= 16 ? one ^ 0x8000u : one));
-    }
-    const float rs32 = 0x1.6a09e6p-3f;
-    const bool m_ok = r < g.m;
-    const uint16_t *xrow = g.x + (m_ok ? r : 0) * g.k;
-    _Float16 *xts_row = xts + r * g.xt_stride;
-    for (int64_t b = pw; b < kb; b += 4) {
-      uint4 xv = make_uint4(0u, 0u, 0u, 0u);
-      if (m_ok) xv = *reinterpret_cast<const uint4 *>(xrow + b * 32 + 8 * grp);
-      const bf16x8 xb = __builtin_bit_cast(bf16x8, xv);
-      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-      const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_lo, xb, zero, 0, 0, 0);
-      const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_hi, xb, zero, 0, 0, 0);
-      uint2 plo, phi;
-      plo.x = f16_bits(lo[0] * rs32) | (f16_bits(lo[1] * rs32) << 16);
-      plo.y = f16_bits(lo[2] * rs32) | (f16_bits(lo[3] * rs32) << 16);
-      phi.x = f16_bits(hi[0] * rs32) | (f16_bits(hi[1] * rs32) << 16);
-      phi.y = f16_bits(hi[2] * rs32) | (f16_bits(hi[3] * rs32) << 16);
-      *reinterpret_cast<uint2 *>(xts_row + b * 32 + 4 * grp) = plo;
-      *reinterpret_cast<uint2 *>(xts_row + b * 32 + 16 + 4 * grp) = phi;
-    }
-  }
-  __syncthreads();
-
-  if (wave < 4) {
-    // decode + MFMA over this wave's K half, weights consumed as they land
-    const _Float16 *xts_row = xts + r * g.xt_stride;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = c0 + i;
-      if (c < c1) {
-        // a lane without a block reads block 0's (finite) activations and a
-        // zero scale, so it adds exact zeros
-        const bool ok = (ok_mask >> i) & 1u;
-        const uint32_t sw = ok ? wr[i].v[4] : 0u;
-        const half2v s0 = scale_pair(sw & 0xFFFFu);
-        const half2v s1 = scale_pair(sw >> 16);
-        const int64_t b = 4 * static_cast<int64_t>(c) + grp;
-        const _Float16 *arow = xts_row + (b < kb ? b : 0) * 32;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const half8 aq =
-              __builtin_bit_cast(half8, *reinterpret_cast<const uint4 *>(arow + 8 * t));
-          const half8 bq = dequant8(wr[i].v[t], t < 2 ? s0 : s1, lut);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq, acc, 0, 0, 0);
-        }
+      for (int i = 0; i < XL; ++i) {
+        const int p = i * 64 + lane;
+        __builtin_amdgcn_global_load_lds((const global_void *)(src + 8 * (p < row_pieces ? p : 0)),
+                                         (lds_void *)(dst + 512 * i), 16, 0, 0);
       }
     }
-    if (kh == 1) red[rg * 64 + lane] = acc;
-  }
-  __syncthreads();
-
-  // add the two K halves in a fixed order and store: lane holds C[4grp+v][r]
-  if (wave < 2 && n_ok) {
-    const floatx4 other = red[rg * 64 + lane];
+    // 0: x requests are out; consumers may start on weights (orders issue only)
+    __builtin_amdgcn_s_barrier();
+    const float lut_lo = g.cb.c[ptid & 15];
+    const float lut_hi = g.cb.c[ptid >> 4];
+    {
+      const uint32_t e = pack_f16x2(lut_lo, lut_hi);
+      uint4 *dst = reinterpret_cast<uint4 *>(lut + ptid * kLutCopies);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = 4 * grp + v;
-      if (m < g.m) g.y[m * g.n + n] = acc[v] + other[v];
+      for (int c = 0; c < kLutCopies / 4; ++c) dst[c] = make_uint4(e, e, e, e);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the LDS-direct loads have landed
+    __syncthreads();  // 1: x rows and pair table in LDS
+    __syncthreads();  // 2: consumers' partial sums in LDS
+    return;
+  }
+
+  // ------------------------------------------------------------ consumers
+  const int chunks = (kb + 3) / 4;
+  // workgroups rotate which wave takes which K range, so that they do not
+  // all touch the same lines at the same moment
+  const int q = (wave + static_cast<int>(blockIdx.x)) % kConsumers;
+  const int c0 = (q * chunks) / kConsumers;
+  const int c_end = ((q + 1) * chunks) / kConsumers;
+  const int n_base = static_cast<int>(blockIdx.x) * kRowsPerWG + r;
+  const uint8_t *wrow[kRowTiles];
+  bool n_ok[kRowTiles];
+#pragma unroll
+  for (int j = 0; j < kRowTiles; ++j) {
+    const int n = n_base + 16 * j;
+    n_ok[j] = n < g.n;
+    wrow[j] = g.w + static_cast<int64_t>(n_ok[j] ? n : 0) * kb * 20;
+  }
+  // rotation operand: MFMA row q stands for output element
+  // pi(q) = 8 (q / 4) + q % 4 (+4 for the second MFMA), column kk for input kk
+  bf16x8 h_lo, h_hi;
+  {
+    const int j_lo = 8 * (r >> 2) + (r & 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = 8 * grp + i;
+      const uint32_t sk = (g.sign_bits >> kk) & 1u;
+      const uint32_t n_lo = (__builtin_popcount(j_lo & kk) & 1) ^ sk;
+      const uint32_t n_hi = (__builtin_popcount((j_lo + 4) & kk) & 1) ^ sk;
+      h_lo[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x3F80u | (n_lo << 15)));
+      h_hi[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x3F80u | (n_hi << 15)));
+    }
+  }
+  __builtin_amdgcn_s_barrier();  // 0
+
+  // every weight block of this wave, chunk by chunk, no branches: a slot
+  // without data re-reads a valid address and gets a zero scale below
+  uint32_t wr[CH][kRowTiles][5];
+  uint32_t ok_mask = 0;  // bit kRowTiles*i + j: weight slot (i, j) is real
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = c0 + i;
+    const int b = 4 * c + grp;
+    const bool b_ok = c < c_end && b < kb;
+#pragma unroll
+    for (int j = 0; j < kRowTiles; ++j) {
+      const bool ok = b_ok && n_ok[j];
+      ok_mask |= static_cast<uint32_t>(ok) << (kRowTiles * i + j);
+      const uint32_t *p = reinterpret_cast<const uint32_t *>(wrow[j] + (ok ? b * 20 : 0));
+#pragma unroll
+      for (int v = 0; v < 5; ++v) wr[i][j][v] = p[v];
+    }
+  }
+  __syncthreads();  // 1
+
+  const uint32_t *my_lut = lut + (lane % kLutCopies);
+  const uint16_t *xs_row = xs + r * xstride;
+  floatx4 acc[kRowTiles];
+#pragma unroll
+  for (int j = 0; j < kRowTiles; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = c0 + i;
+    // 1. rotated activations of blocks 4c + t (block 0 past the end: finite,
+    //    and it meets zero weights)
+    half8 a[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int b = 4 * c + t;
+      const int col = (c < c_end && b < kb) ? 32 * b : 0;
+      const bf16x8 xb8 =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(xs_row + col + 8 * grp));
+      const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_lo, xb8, zero, 0, 0, 0);
+      const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_hi, xb8, zero, 0, 0, 0);
+      a[t] = __builtin_bit_cast(half8, make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
+                                                  pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])));
+    }
+#pragma unroll
+    for (int j = 0; j < kRowTiles; ++j) {
+      // 2. word g of every block of the chunk into lane group g
+      uint32_t codes[4] = {wr[i][j][0], wr[i][j][1], wr[i][j][2], wr[i][j][3]};
+      const uint32_t sw = ((ok_mask >> (kRowTiles * i + j)) & 1u) ? wr[i][j][4] : 0u;
+      uint32_t scales[4] = {sw, sw, sw, sw};
+      transpose4(codes);
+      transpose4(scales);
+      // 3. decode elements 8g..8g+7 of block 4c + t (half g / 2) and multiply
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const half2v sc = scale_pair(grp < 2 ? (scales[t] & 0xFFFFu) : (scales[t] >> 16));
+        const half8 bq = dequant8(codes[t], sc, my_lut);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bq, acc[j], 0, 0, 0);
+      }
+    }
+  }
+
+  // the consumers' partial sums, in wave order; lane holds C[4grp+v][r]
+#pragma unroll
+  for (int j = 0; j < kRowTiles; ++j) red[wave][j][lane] = acc[j];
+  __syncthreads();  // 2
+  if (wave < kRowTiles) {
+    floatx4 s = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < kConsumers; ++w) s += red[w][wave][lane];
+    const int n = n_base + 16 * wave;
+    if (n < g.n) {
+      const float rs32 = 0x1.6a09e6p-3f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * grp + v;
+        if (m < g.m) g.y[static_cast<int64_t>(m) * g.n + n] = s[v] * rs32;
+      }
     }
   }
 }
 
-template <int CH>
-hipError_t launch_ch(const SkinnyArgs &a, hipStream_t s) {
-  const size_t lds = kLutBytes + kRedBytes + static_cast<size_t>(16) * a.xt_stride * 2;
-  static bool attr_set = false;  // raising the limit is idempotent; races are harmless
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&skinny_kernel<CH>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(kSkinnyMaxLds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+template <int CH, int XL>
+hipError_t launch_cfg(const SkinnyArgs &a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((a.n + kRowsPerWG - 1) / kRowsPerWG);
-  hipLaunchKernelGGL(skinny_kernel<CH>, dim3(grid), dim3(512), lds, s, a);
+  hipLaunchKernelGGL((skinny_kernel<CH, XL>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+template <int CH>
+hipError_t launch_ch(const SkinnyArgs &a, int xl, hipStream_t s) {
+  switch (xl) {  // loads per lane per x row: ceil(k / 8 / 64)
+    case 1: return launch_cfg<CH, 1>(a, s);
+    case 2: return launch_cfg<CH, 2>(a, s);
+    case 3: return launch_cfg<CH, 3>(a, s);
+    case 4: return launch_cfg<CH, 4>(a, s);
+    case 5: return launch_cfg<CH, 5>(a, s);
+    case 6: return launch_cfg<CH, 6>(a, s);
+    case 7: return launch_cfg<CH, 7>(a, s);
+    case 8: return launch_cfg<CH, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-// LDS row stride (halves) of the rotated activations: the row length padded
-// so that consecutive rows start 4 banks apart (16-lane 128-bit reads of 16
-// different rows then touch 64 distinct banks).
-int32_t skinny_xt_stride(int64_t k) {
-  const int64_t dwords = ((k / 2 + 63) / 64) * 64 + 4;
-  return static_cast<int32_t>(2 * dwords);
-}
-
-bool skinny_fits(int64_t m, int64_t k) {
-  if (m < 1 || m > 16 || k < 32 || k > 4096) return false;
-  const size_t lds = kLutBytes + kRedBytes + static_cast<size_t>(16) * skinny_xt_stride(k) * 2;
-  return lds <= kSkinnyMaxLds;
+bool skinny_fits(int64_t m, int64_t k, int64_t n) {
+  // 32-bit offsets inside the kernel: the packed matrix stays below 2 GiB
+  return m >= 1 && m <= 16 && k >= 32 && k <= kMaxK && n >= 1 &&
+         n * (k / 32) * 20 < (int64_t{1} << 31);
 }
 
 hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
@@ -236,31 +316,19 @@ hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t 
   a.x = x;
   a.w = packed;
   a.y = y;
-  a.m = m;
-  a.n = n;
-  a.k = k;
-  a.xt_stride = skinny_xt_stride(k);
+  a.m = static_cast<int32_t>(m);
+  a.n = static_cast<int32_t>(n);
+  a.kb = static_cast<int32_t>(k / 32);
   a.sign_bits = sign_bits;
   a.cb = codebook();
-  const int64_t chunks = (k / 32 + 3) / 4;
-  const int64_t half = (chunks + 1) / 2;
-  switch (half) {
-    case 1: return launch_ch<1>(a, s);
-    case 2: return launch_ch<2>(a, s);
-    case 3: return launch_ch<3>(a, s);
-    case 4: return launch_ch<4>(a, s);
-    case 5: return launch_ch<5>(a, s);
-    case 6: return launch_ch<6>(a, s);
-    case 7: return launch_ch<7>(a, s);
-    case 8: return launch_ch<8>(a, s);
-    case 9: return launch_ch<9>(a, s);
-    case 10: return launch_ch<10>(a, s);
-    case 11: return launch_ch<11>(a, s);
-    case 12: return launch_ch<12>(a, s);
-    case 13: return launch_ch<13>(a, s);
-    case 14: return launch_ch<14>(a, s);
-    case 15: return launch_ch<15>(a, s);
-    case 16: return launch_ch<16>(a, s);
+  const int64_t chunks = (k / 32 + 3) / 4;                          // <= 32
+  const int64_t per_wave = (chunks + kConsumers - 1) / kConsumers;  // <= 4
+  const int xl = static_cast<int>((k / 8 + 63) / 64);               // <= 8
+  switch (per_wave) {
+    case 1: return launch_ch<1>(a, xl, s);
+    case 2: return launch_ch<2>(a, xl, s);
+    case 3: return launch_ch<3>(a, xl, s);
+    case 4: return launch_ch<4>(a, xl, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -42,7 +42,7 @@ hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64
                         hipStream_t s);
 
 // Single-kernel path for m <= 16 (rotation fused, no workspace).
-bool skinny_fits(int64_t m, int64_t k);
+bool skinny_fits(int64_t m, int64_t k, int64_t n);
 hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
                          int64_t n, uint32_t sign_bits, float *y, hipStream_t s);
 

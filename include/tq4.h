@@ -93,8 +93,8 @@ int tq4_act_rht(const uint16_t *x_bf16, int64_t m, int64_t k, uint32_t sign_bits
                 uint16_t *xt_f16, void *stream);
 
 /* Workspace bytes that suffice for both tq4_linear and tq4_linear_rotated at
- * these sizes (0 if the sizes are invalid, or if neither needs scratch, e.g.
- * m <= 16).  No initial contents are required. */
+ * these sizes (0 if the sizes are invalid or the call is empty).  No initial
+ * contents are required. */
 size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n);
 
 /* The on-the-fly dequantizing linear layer (model card, section Running it):
@@ -105,7 +105,7 @@ size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n);
  *   y       : [m, n] fp32, device, 4-byte aligned, overwritten
  *   workspace / workspace_bytes : device scratch of at least
  *             tq4_linear_workspace_size(m, k, n) bytes, 256-byte aligned
- *             (may be NULL when that size is 0)
+ *             (may be NULL when that size is 0, as for m <= 16)
  * The rotation is applied to the activations (R x, see tq4_act_rht) and the
  * product runs on 16-bit MFMA with fp32 accumulation; results are
  * deterministic.  For m <= 16 and k <= 4096 this is a single kernel.
