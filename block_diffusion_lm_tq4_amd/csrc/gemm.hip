@@ -41,6 +41,8 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
 
 enum Mode { kDense = 0, kMoEUp = 1, kMoEDown = 2 };
 
@@ -57,19 +59,25 @@ struct GemmArgs {
   int32_t topk;
   int32_t ksplit;
   int32_t chunks;            // ceil(k / 128)
+  int32_t tiles_m, tiles_n;  // dense: workgroup tiles along m and n
   Codebook cb;
 };
+
+constexpr int kWaves = 4;          // waves per workgroup, side by side along n
+constexpr int kLutCopies = 8;      // pair-table copies (lane % 8 picks one)
+constexpr int kChunkBytes = 256;   // one fp16 activation row over one chunk (128 k)
 
 __device__ inline uint32_t f16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(f)));
 }
 
 // 8 dequantized weights (one codes word) times the half-block scale pair.
+// `lut` points at this lane's copy of the pair table: entry e is lut[e * kLutCopies].
 __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *lut) {
-  const half2v p0 = __builtin_bit_cast(half2v, lut[codes & 0xFFu]) * scale;
-  const half2v p1 = __builtin_bit_cast(half2v, lut[(codes >> 8) & 0xFFu]) * scale;
-  const half2v p2 = __builtin_bit_cast(half2v, lut[(codes >> 16) & 0xFFu]) * scale;
-  const half2v p3 = __builtin_bit_cast(half2v, lut[codes >> 24]) * scale;
+  const half2v p0 = __builtin_bit_cast(half2v, lut[(codes & 0xFFu) * kLutCopies]) * scale;
+  const half2v p1 = __builtin_bit_cast(half2v, lut[((codes >> 8) & 0xFFu) * kLutCopies]) * scale;
+  const half2v p2 = __builtin_bit_cast(half2v, lut[((codes >> 16) & 0xFFu) * kLutCopies]) * scale;
+  const half2v p3 = __builtin_bit_cast(half2v, lut[(codes >> 24) * kLutCopies]) * scale;
   half8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
@@ -87,32 +95,41 @@ __device__ inline half2v scale_pair(uint32_t bf16_bits) {
 struct WRaw {
   uint32_t v[5];
 };
-struct ARaw {
-  uint4 v[4];
-};
 
-template <int MSUB, int NSUB, int WM, int WN, int MODE>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
-  constexpr int WG_M = 16 * MSUB * WM;
-  constexpr int WG_N = 16 * NSUB * WN;
+template <int MSUB, int NSUB, int MODE>
+__global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
+  constexpr int TM = 16 * MSUB;           // activation rows per workgroup
+  constexpr int TN = 16 * NSUB * kWaves;  // weight rows per workgroup
 
-  __shared__ uint32_t lut[256];
+  // Activation tile of one chunk, double buffered.  Row r occupies 256 bytes
+  // (16 slots of 8 halves); global slot s of row r is stored in slot
+  // s ^ (r % 16), so the fragment reads below (16 rows, one slot each) fall
+  // on 16 distinct 16-byte bank groups.
+  __shared__ __attribute__((aligned(16))) uint8_t abuf0[TM * kChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf1[TM * kChunkBytes];
+  __shared__ uint32_t lut[256 * kLutCopies];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
   const int r = lane % 16;
   const int grp = lane / 16;
-  const int wave_m = wave / WN;
-  const int wave_n = wave % WN;
 
   // ---- which tile -------------------------------------------------------
-  int64_t m_base = 0;        // first output row of the workgroup tile
+  int64_t m_base = 0;        // first activation row of the workgroup tile
   int64_t rows_valid = g.m;  // rows of this tile that exist (relative to m_base)
+  int64_t n_base = 0;
   const uint8_t *wmat = g.w;
   int split = 0;
   if constexpr (MODE == kDense) {
-    m_base = static_cast<int64_t>(blockIdx.y) * WG_M;
+    // Consecutive workgroup ids go to different XCDs (round robin over 8);
+    // renumber so that each XCD works on a contiguous range of tiles (a band
+    // of activation rows against all weight rows), which its own L2 serves.
+    const int tiles = g.tiles_m * g.tiles_n;
+    int t = static_cast<int>(blockIdx.x);
+    if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
+    m_base = static_cast<int64_t>(t / g.tiles_n) * TM;
+    n_base = static_cast<int64_t>(t % g.tiles_n) * TN;
     rows_valid = g.m - m_base;
     split = blockIdx.z;
   } else {
@@ -121,45 +138,72 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     m_base = t.row0;
     rows_valid = t.rows;
     wmat = g.w + static_cast<int64_t>(t.expert) * g.expert_stride;
+    n_base = static_cast<int64_t>(blockIdx.x) * TN;
   }
-  const int64_t n_base = static_cast<int64_t>(blockIdx.x) * WG_N;
 
-  // ---- codebook pair table ------------------------------------------------
-  for (int i = tid; i < 256; i += 64 * WM * WN)
-    lut[i] = f16_bits(g.cb.c[i & 15]) | (f16_bits(g.cb.c[i >> 4]) << 16);
-  __syncthreads();
+  // ---- codebook pair table, kLutCopies interleaved copies -----------------
+  for (int i = tid; i < 256 * kLutCopies; i += 64 * kWaves) {
+    const int e = i / kLutCopies;
+    lut[i] = f16_bits(g.cb.c[e & 15]) | (f16_bits(g.cb.c[e >> 4]) << 16);
+  }
+  const uint32_t *lutp = lut + (lane % kLutCopies);
 
-  const int64_t kb = g.k / 32;
+  const int kb = static_cast<int>(g.k / 32);
   const int c_begin = static_cast<int>((static_cast<int64_t>(g.chunks) * split) / g.ksplit);
   const int c_end = static_cast<int>((static_cast<int64_t>(g.chunks) * (split + 1)) / g.ksplit);
 
-  // activation row pointers and weight row pointers for this lane
-  const uint16_t *arow[MSUB];
-  bool a_ok[MSUB];
+  // ---- activation rows this lane copies into LDS ---------------------------
+  // A tile is TM rows x 256 bytes = 4*MSUB loads of 1 KB (4 rows each); wave
+  // w issues loads w*MSUB .. w*MSUB+MSUB-1.  Lane L of load q fills LDS row
+  // 4q + L/16, slot L%16, i.e. global slot (L%16) ^ (row%16) of that row.
+  // Rows past the tile's end copy a valid row (their outputs are not stored).
+  const uint16_t *asrc[MSUB];
+  int aslot[MSUB];
 #pragma unroll
   for (int i = 0; i < MSUB; ++i) {
-    const int64_t local = wave_m * (16 * MSUB) + 16 * i + r;
-    a_ok[i] = local < rows_valid;
-    int64_t src_row = 0;
-    if (a_ok[i]) {
-      if constexpr (MODE == kDense) {
-        src_row = m_base + local;
-      } else if constexpr (MODE == kMoEUp) {
-        src_row = g.perm[m_base + local] / g.topk;
-      } else {
-        src_row = m_base + local;
-      }
+    const int row = 4 * (wave * MSUB + i) + lane / 16;
+    const int64_t local = row < rows_valid ? row : 0;
+    int64_t src_row;
+    if constexpr (MODE == kMoEUp) {
+      src_row = g.perm[m_base + local] / g.topk;
+    } else {
+      src_row = m_base + local;
     }
-    arow[i] = g.a + src_row * g.k;
+    asrc[i] = g.a + src_row * g.k;
+    aslot[i] = (lane % 16) ^ (row % 16);
   }
+  auto issue_a = [&](int c, uint8_t *buf) {
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i) {
+      const int blk = 4 * c + aslot[i] / 4;
+      const uint16_t *src = asrc[i] + (blk < kb ? 128 * c + 8 * aslot[i] : 0);
+      __builtin_amdgcn_global_load_lds((const global_void *)src,
+                                       (lds_void *)(buf + (wave * MSUB + i) * 4 * kChunkBytes),
+                                       16, 0, 0);
+    }
+  };
+
+  // ---- weight rows of this lane: 16*NSUB rows per wave ----------------------
   const uint8_t *wrow[NSUB];
   bool w_ok[NSUB];
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
-    const int64_t n = n_base + wave_n * (16 * NSUB) + 16 * j + r;
+    const int64_t n = n_base + wave * (16 * NSUB) + 16 * j + r;
     w_ok[j] = n < g.n;
     wrow[j] = wmat + (w_ok[j] ? n : 0) * kb * 20;
   }
+  // Lane group g takes block 4c+g of each row.  Blocks past k and rows past n
+  // read block 0 of a valid row and get a zero scale word, so they add 0.
+  auto load_w = [&](int c, WRaw (&wr)[NSUB]) {
+    const int b = 4 * c + grp;
+    const bool b_ok = b < kb;
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      const uint32_t *p = reinterpret_cast<const uint32_t *>(wrow[j] + (b_ok ? b : 0) * 20);
+#pragma unroll
+      for (int q = 0; q < 5; ++q) wr[j].v[q] = p[q];
+    }
+  };
 
   floatx4 acc[MSUB][NSUB];
 #pragma unroll
@@ -167,48 +211,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < NSUB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_chunk = [&](int c, WRaw (&wr)[NSUB], ARaw (&ar)[MSUB]) {
-    const int64_t b = 4 * static_cast<int64_t>(c) + grp;
-    const bool b_ok = b < kb;
-#pragma unroll
-    for (int j = 0; j < NSUB; ++j) {
-      if (b_ok && w_ok[j]) {
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(wrow[j] + b * 20);
-#pragma unroll
-        for (int q = 0; q < 5; ++q) wr[j].v[q] = p[q];
-      } else {
-#pragma unroll
-        for (int q = 0; q < 5; ++q) wr[j].v[q] = 0u;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < MSUB; ++i) {
-      if (b_ok && a_ok[i]) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(arow[i] + b * 32);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ar[i].v[q] = p[q];
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ar[i].v[q] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-
-  auto compute_chunk = [&](const WRaw (&wr)[NSUB], const ARaw (&ar)[MSUB]) {
+  auto compute_chunk = [&](const WRaw (&wr)[NSUB], const uint8_t *abase, int c) {
+    const bool b_ok = 4 * c + grp < kb;
     half2v sc[NSUB][2];
 #pragma unroll
     for (int j = 0; j < NSUB; ++j) {
-      sc[j][0] = scale_pair(wr[j].v[4] & 0xFFFFu);
-      sc[j][1] = scale_pair(wr[j].v[4] >> 16);
+      const uint32_t sw = (b_ok && w_ok[j]) ? wr[j].v[4] : 0u;
+      sc[j][0] = scale_pair(sw & 0xFFFFu);
+      sc[j][1] = scale_pair(sw >> 16);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       half8 bq[NSUB];
 #pragma unroll
-      for (int j = 0; j < NSUB; ++j) bq[j] = dequant8(wr[j].v[t], sc[j][t >> 1], lut);
+      for (int j = 0; j < NSUB; ++j) bq[j] = dequant8(wr[j].v[t], sc[j][t >> 1], lutp);
+      const int slot = (4 * grp + t) ^ r;
 #pragma unroll
       for (int i = 0; i < MSUB; ++i) {
-        const half8 aq = __builtin_bit_cast(half8, ar[i].v[t]);
+        const half8 aq =
+            *reinterpret_cast<const half8 *>(abase + (16 * i + r) * kChunkBytes + 16 * slot);
 #pragma unroll
         for (int j = 0; j < NSUB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq[j], acc[i][j], 0, 0, 0);
@@ -216,19 +237,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     }
   };
 
+  // Two-stage pipeline: while chunk c is multiplied out of one buffer, chunk
+  // c+1 streams into the other (the loop is unrolled by two so that each
+  // step names its buffers statically).
+  auto step = [&](int c, WRaw (&wr)[NSUB], WRaw (&wn)[NSUB], const uint8_t *cur, uint8_t *nxt) {
+    if (c + 1 < c_end) {
+      issue_a(c + 1, nxt);
+      load_w(c + 1, wn);
+    }
+    compute_chunk(wr, cur, c);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // next chunk landed; this buffer is free again
+  };
   if (c_begin < c_end) {
-    WRaw wr_next[NSUB];
-    ARaw ar_next[MSUB];
-    load_chunk(c_begin, wr_next, ar_next);
-    for (int c = c_begin; c < c_end; ++c) {
-      WRaw wr[NSUB];
-      ARaw ar[MSUB];
-#pragma unroll
-      for (int j = 0; j < NSUB; ++j) wr[j] = wr_next[j];
-#pragma unroll
-      for (int i = 0; i < MSUB; ++i) ar[i] = ar_next[i];
-      if (c + 1 < c_end) load_chunk(c + 1, wr_next, ar_next);
-      compute_chunk(wr, ar);
+    WRaw w0[NSUB], w1[NSUB];
+    issue_a(c_begin, abuf0);
+    load_w(c_begin, w0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // pair table and first activation chunk in LDS
+    for (int c = c_begin; c < c_end; c += 2) {
+      step(c, w0, w1, abuf0, abuf1);
+      if (c + 1 < c_end) step(c + 1, w1, w0, abuf1, abuf0);
     }
   }
 
@@ -239,10 +268,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
-        const int64_t n = n_base + wave_n * (16 * NSUB) + 16 * j + r;
+        const int64_t n = n_base + wave * (16 * NSUB) + 16 * j + r;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int64_t m = m_base + wave_m * (16 * MSUB) + 16 * i + 4 * grp + v;
+          const int64_t m = m_base + 16 * i + 4 * grp + v;
           if (m < g.m && n < g.n) dst[m * g.n + n] = acc[i][j][v];
         }
       }
@@ -251,10 +280,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
       for (int j = 0; j < NSUB; ++j) {
-        const int64_t n = n_base + wave_n * (16 * NSUB) + 16 * j + r;
+        const int64_t n = n_base + wave * (16 * NSUB) + 16 * j + r;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int64_t local = wave_m * (16 * MSUB) + 16 * i + 4 * grp + v;
+          const int64_t local = 16 * i + 4 * grp + v;
           if (local < rows_valid && n < g.n) {
             float val = acc[i][j][v];
             if constexpr (MODE == kMoEUp) {
@@ -278,25 +307,24 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__res
   y[i] = s;
 }
 
-template <int MSUB, int NSUB, int WM, int WN, int MODE>
+template <int MSUB, int NSUB, int MODE>
 hipError_t launch_cfg(const GemmArgs &g, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<MSUB, NSUB, WM, WN, MODE>), grid, dim3(64 * WM * WN), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<MSUB, NSUB, MODE>), grid, dim3(64 * kWaves), 0, s, g);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t dispatch(int msub, int nsub, int wm, int wn, const GemmArgs &g, dim3 grid,
-                    hipStream_t s) {
-  if (wm == 1 && wn == 4 && nsub == 2) {
+hipError_t dispatch(int msub, int nsub, const GemmArgs &g, dim3 grid, hipStream_t s) {
+  if (nsub == 2) {
     switch (msub) {
-      case 1: return launch_cfg<1, 2, 1, 4, MODE>(g, grid, s);
-      case 2: return launch_cfg<2, 2, 1, 4, MODE>(g, grid, s);
-      case 3: return launch_cfg<3, 2, 1, 4, MODE>(g, grid, s);
-      case 4: return launch_cfg<4, 2, 1, 4, MODE>(g, grid, s);
+      case 1: return launch_cfg<1, 2, MODE>(g, grid, s);
+      case 2: return launch_cfg<2, 2, MODE>(g, grid, s);
+      case 3: return launch_cfg<3, 2, MODE>(g, grid, s);
+      case 4: return launch_cfg<4, 2, MODE>(g, grid, s);
       default: break;
     }
   }
-  if (wm == 2 && wn == 2 && msub == 4 && nsub == 4) return launch_cfg<4, 4, 2, 2, MODE>(g, grid, s);
+  if (nsub == 4 && msub == 8) return launch_cfg<8, 4, MODE>(g, grid, s);
   return hipErrorInvalidValue;
 }
 
@@ -305,17 +333,15 @@ hipError_t dispatch(int msub, int nsub, int wm, int wn, const GemmArgs &g, dim3 
 DensePlan plan_dense(int64_t m, int64_t k, int64_t n) {
   DensePlan p{};
   p.chunks = (k / 32 + 3) / 4;
+  p.waves_m = 1;
+  p.waves_n = 4;
   if (m <= 64) {
     p.msub = static_cast<int>((m + 15) / 16);
     if (p.msub < 1) p.msub = 1;
     p.nsub = 2;
-    p.waves_m = 1;
-    p.waves_n = 4;
   } else {
-    p.msub = 4;
+    p.msub = 8;
     p.nsub = 4;
-    p.waves_m = 2;
-    p.waves_n = 2;
   }
   const int64_t wg_m = 16 * p.msub * p.waves_m;
   const int64_t wg_n = 16 * p.nsub * p.waves_n;
@@ -347,10 +373,11 @@ hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64
   g.k = k;
   g.ksplit = p.ksplit;
   g.chunks = static_cast<int32_t>(p.chunks);
+  g.tiles_m = static_cast<int32_t>(p.m_tiles);
+  g.tiles_n = static_cast<int32_t>(p.n_tiles);
   g.cb = codebook();
-  const dim3 grid(static_cast<unsigned>(p.n_tiles), static_cast<unsigned>(p.m_tiles),
-                  static_cast<unsigned>(p.ksplit));
-  hipError_t e = dispatch<kDense>(p.msub, p.nsub, p.waves_m, p.waves_n, g, grid, s);
+  const dim3 grid(static_cast<unsigned>(p.n_tiles * p.m_tiles), 1, static_cast<unsigned>(p.ksplit));
+  hipError_t e = dispatch<kDense>(p.msub, p.nsub, g, grid, s);
   if (e != hipSuccess || p.ksplit == 1) return e;
   const int64_t mn = m * n;
   hipLaunchKernelGGL(reduce_partials_kernel, dim3(static_cast<unsigned>((mn + 255) / 256)),
@@ -392,8 +419,8 @@ hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_
   const int64_t wg_n = 16 * p.nsub * p.waves_n;
   const dim3 grid(static_cast<unsigned>((n + wg_n - 1) / wg_n), static_cast<unsigned>(p.max_tiles),
                   1);
-  if (mode == 0) return dispatch<kMoEUp>(p.msub, p.nsub, p.waves_m, p.waves_n, g, grid, s);
-  return dispatch<kMoEDown>(p.msub, p.nsub, p.waves_m, p.waves_n, g, grid, s);
+  if (mode == 0) return dispatch<kMoEUp>(p.msub, p.nsub, g, grid, s);
+  return dispatch<kMoEDown>(p.msub, p.nsub, g, grid, s);
 }
 
 }  // namespace tq4
