@@ -64,7 +64,6 @@ struct GemmArgs {
 };
 
 constexpr int kWaves = 4;          // waves per workgroup, side by side along n
-constexpr int kLutCopies = 8;      // pair-table copies (lane % 8 picks one)
 constexpr int kChunkBytes = 256;   // one fp16 activation row over one chunk (128 k)
 
 __device__ inline uint32_t f16_bits(float f) {
@@ -72,12 +71,13 @@ __device__ inline uint32_t f16_bits(float f) {
 }
 
 // 8 dequantized weights (one codes word) times the half-block scale pair.
-// `lut` points at this lane's copy of the pair table: entry e is lut[e * kLutCopies].
+// `lut` points at this lane's copy of the pair table: entry e is lut[e * LUTC].
+template <int LUTC>
 __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *lut) {
-  const half2v p0 = __builtin_bit_cast(half2v, lut[(codes & 0xFFu) * kLutCopies]) * scale;
-  const half2v p1 = __builtin_bit_cast(half2v, lut[((codes >> 8) & 0xFFu) * kLutCopies]) * scale;
-  const half2v p2 = __builtin_bit_cast(half2v, lut[((codes >> 16) & 0xFFu) * kLutCopies]) * scale;
-  const half2v p3 = __builtin_bit_cast(half2v, lut[(codes >> 24) * kLutCopies]) * scale;
+  const half2v p0 = __builtin_bit_cast(half2v, lut[(codes & 0xFFu) * LUTC]) * scale;
+  const half2v p1 = __builtin_bit_cast(half2v, lut[((codes >> 8) & 0xFFu) * LUTC]) * scale;
+  const half2v p2 = __builtin_bit_cast(half2v, lut[((codes >> 16) & 0xFFu) * LUTC]) * scale;
+  const half2v p3 = __builtin_bit_cast(half2v, lut[(codes >> 24) * LUTC]) * scale;
   half8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
@@ -96,7 +96,10 @@ struct WRaw {
   uint32_t v[5];
 };
 
-template <int MSUB, int NSUB, int MODE>
+// LUTC copies of the pair table are interleaved (entry e of copy q at
+// e * LUTC + q; lane L uses copy L % LUTC), so that random lookups by the
+// lanes of a wave spread over the LDS banks.
+template <int MSUB, int NSUB, int LUTC, int MODE>
 __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
   constexpr int TM = 16 * MSUB;           // activation rows per workgroup
   constexpr int TN = 16 * NSUB * kWaves;  // weight rows per workgroup
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
   // on 16 distinct 16-byte bank groups.
   __shared__ __attribute__((aligned(16))) uint8_t abuf0[TM * kChunkBytes];
   __shared__ __attribute__((aligned(16))) uint8_t abuf1[TM * kChunkBytes];
-  __shared__ uint32_t lut[256 * kLutCopies];
+  __shared__ uint32_t lut[256 * LUTC];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
@@ -141,12 +144,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
     n_base = static_cast<int64_t>(blockIdx.x) * TN;
   }
 
-  // ---- codebook pair table, kLutCopies interleaved copies -----------------
-  for (int i = tid; i < 256 * kLutCopies; i += 64 * kWaves) {
-    const int e = i / kLutCopies;
+  // ---- codebook pair table, LUTC interleaved copies -----------------------
+  for (int i = tid; i < 256 * LUTC; i += 64 * kWaves) {
+    const int e = i / LUTC;
     lut[i] = f16_bits(g.cb.c[e & 15]) | (f16_bits(g.cb.c[e >> 4]) << 16);
   }
-  const uint32_t *lutp = lut + (lane % kLutCopies);
+  const uint32_t *lutp = lut + (lane % LUTC);
 
   const int kb = static_cast<int>(g.k / 32);
   const int c_begin = static_cast<int>((static_cast<int64_t>(g.chunks) * split) / g.ksplit);
@@ -205,6 +208,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
     }
   };
 
+  // An (empty) use of an accumulation register lets the compiler keep the
+  // accumulators in them for the whole loop instead of copying them in and
+  // out of ordinary vector registers around every MFMA.
+  asm volatile("" ::"a"(0));
   floatx4 acc[MSUB][NSUB];
 #pragma unroll
   for (int i = 0; i < MSUB; ++i)
@@ -224,7 +231,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
     for (int t = 0; t < 4; ++t) {
       half8 bq[NSUB];
 #pragma unroll
-      for (int j = 0; j < NSUB; ++j) bq[j] = dequant8(wr[j].v[t], sc[j][t >> 1], lutp);
+      for (int j = 0; j < NSUB; ++j) bq[j] = dequant8<LUTC>(wr[j].v[t], sc[j][t >> 1], lutp);
       const int slot = (4 * grp + t) ^ r;
 #pragma unroll
       for (int i = 0; i < MSUB; ++i) {
@@ -234,6 +241,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < NSUB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq[j], acc[i][j], 0, 0, 0);
       }
+      // with large tiles, keep one step's operands live at a time
+      if constexpr (MSUB * NSUB >= 64) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -255,10 +264,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
     load_w(c_begin, w0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // pair table and first activation chunk in LDS
-    for (int c = c_begin; c < c_end; c += 2) {
+    int c = c_begin;
+    for (; c + 1 < c_end; c += 2) {
       step(c, w0, w1, abuf0, abuf1);
-      if (c + 1 < c_end) step(c + 1, w1, w0, abuf1, abuf0);
+      step(c + 1, w1, w0, abuf1, abuf0);
     }
+    if (c < c_end) step(c, w0, w1, abuf0, abuf1);
   }
 
   // ---- epilogue: lane holds C[4*grp + v][r] of every 16x16 tile ----------
@@ -307,9 +318,9 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__res
   y[i] = s;
 }
 
-template <int MSUB, int NSUB, int MODE>
+template <int MSUB, int NSUB, int LUTC, int MODE>
 hipError_t launch_cfg(const GemmArgs &g, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<MSUB, NSUB, MODE>), grid, dim3(64 * kWaves), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<MSUB, NSUB, LUTC, MODE>), grid, dim3(64 * kWaves), 0, s, g);
   return hipGetLastError();
 }
 
@@ -317,14 +328,16 @@ template <int MODE>
 hipError_t dispatch(int msub, int nsub, const GemmArgs &g, dim3 grid, hipStream_t s) {
   if (nsub == 2) {
     switch (msub) {
-      case 1: return launch_cfg<1, 2, MODE>(g, grid, s);
-      case 2: return launch_cfg<2, 2, MODE>(g, grid, s);
-      case 3: return launch_cfg<3, 2, MODE>(g, grid, s);
-      case 4: return launch_cfg<4, 2, MODE>(g, grid, s);
+      case 1: return launch_cfg<1, 2, 8, MODE>(g, grid, s);
+      case 2: return launch_cfg<2, 2, 8, MODE>(g, grid, s);
+      case 3: return launch_cfg<3, 2, 8, MODE>(g, grid, s);
+      case 4: return launch_cfg<4, 2, 8, MODE>(g, grid, s);
       default: break;
     }
   }
-  if (nsub == 4 && msub == 8) return launch_cfg<8, 4, MODE>(g, grid, s);
+  if constexpr (MODE == kDense) {
+    if (nsub == 4 && msub == 8) return launch_cfg<8, 4, 32, MODE>(g, grid, s);
+  }
   return hipErrorInvalidValue;
 }
 
