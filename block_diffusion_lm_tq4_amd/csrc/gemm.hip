@@ -208,10 +208,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
     }
   };
 
-  // An (empty) use of an accumulation register lets the compiler keep the
-  // accumulators in them for the whole loop instead of copying them in and
-  // out of ordinary vector registers around every MFMA.
-  asm volatile("" ::"a"(0));
+  // For large tiles, an (empty) use of an accumulation register lets the
+  // compiler keep the accumulators in them for the whole loop instead of
+  // copying them in and out of ordinary vector registers around every MFMA.
+  if constexpr (MSUB * NSUB >= 32) asm volatile("" ::"a"(0));
   floatx4 acc[MSUB][NSUB];
 #pragma unroll
   for (int i = 0; i < MSUB; ++i)

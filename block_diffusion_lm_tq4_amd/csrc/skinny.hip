@@ -68,20 +68,21 @@ struct SkinnyArgs {
   Codebook cb;
 };
 
-__device__ inline uint32_t f16_bits(float f) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(f)));
-}
+typedef float float2v __attribute__((ext_vector_type(2)));
 
+// two fp32 values to a packed fp16 pair, round to nearest even (one
+// v_cvt_pk_f16_f32)
 __device__ inline uint32_t pack_f16x2(float lo, float hi) {
-  return f16_bits(lo) | (f16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, half2v));
 }
 
-// `lut` points at this lane's copy: entry e is lut[e * kLutCopies].
+// `lut` points at this lane's copy: entry e is lut[e * C].
+template <int C = kLutCopies>
 __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *lut) {
-  const half2v p0 = __builtin_bit_cast(half2v, lut[(codes & 0xFFu) * kLutCopies]) * scale;
-  const half2v p1 = __builtin_bit_cast(half2v, lut[((codes >> 8) & 0xFFu) * kLutCopies]) * scale;
-  const half2v p2 = __builtin_bit_cast(half2v, lut[((codes >> 16) & 0xFFu) * kLutCopies]) * scale;
-  const half2v p3 = __builtin_bit_cast(half2v, lut[(codes >> 24) * kLutCopies]) * scale;
+  const half2v p0 = __builtin_bit_cast(half2v, lut[(codes & 0xFFu) * C]) * scale;
+  const half2v p1 = __builtin_bit_cast(half2v, lut[((codes >> 8) & 0xFFu) * C]) * scale;
+  const half2v p2 = __builtin_bit_cast(half2v, lut[((codes >> 16) & 0xFFu) * C]) * scale;
+  const half2v p3 = __builtin_bit_cast(half2v, lut[(codes >> 24) * C]) * scale;
   half8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
@@ -89,11 +90,15 @@ __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *l
 }
 
 __device__ inline half2v scale_pair(uint32_t bf16_bits) {
-  const _Float16 h = static_cast<_Float16>(__uint_as_float(bf16_bits << 16));
-  half2v r;
-  r[0] = h;
-  r[1] = h;
-  return r;
+  const float f = __uint_as_float(bf16_bits << 16);
+  return __builtin_convertvector((float2v){f, f}, half2v);
+}
+
+// the scale of half `h` (0: elements 0-15, 1: 16-31) of a block from its
+// scale word (S0 in the low 16 bits, S1 in the high 16 bits)
+__device__ inline half2v half_scale(uint32_t word, int h) {
+  const float f = __uint_as_float((word << (16 - 16 * h)) & 0xFFFF0000u);
+  return __builtin_convertvector((float2v){f, f}, half2v);
 }
 
 // 4x4 transpose across the lane groups (rows of 16 lanes): on entry lane
@@ -280,6 +285,194 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-direct variant, for K a multiple of 128 up to kDmaMaxK.  Measured on
+// this shape, what bounds the kernel is how fast a compute unit takes in its
+// bytes: the weights of its 32 rows plus all of x, which every workgroup
+// needs.  LDS-direct loads of 16 bytes per lane, each instruction covering
+// 1 KB of consecutive memory, take those in markedly faster than loads into
+// registers, so this variant stages everything in LDS, chunk by chunk: a
+// chunk slot holds the chunk's slice of x (16 rows x 256 bytes, its 16-byte
+// parts XOR-swizzled by row so that fragment reads hit distinct banks) and
+// its weights (32 rows x 80 bytes).
+//
+//  * kDmaProducers waves keep the loads going: producer p takes chunks p,
+//    p + kDmaProducers, ..., keeps up to three of them in flight, and as each
+//    lands (its loads retire in issue order) raises that chunk's LDS flag.
+//  * kDmaConsumers waves take chunks round robin; each waits for the chunk's
+//    flag, rotates the x blocks (two bf16 MFMAs per block against the +-1
+//    matrix, as in skinny_kernel), decodes its lane's code words through the
+//    pair table and accumulates with f16 MFMAs.  Consumers issue no
+//    vector-memory loads, so nothing they do waits on the stream.
+constexpr int kDmaProducers = 4;
+constexpr int kDmaConsumers = 8;
+constexpr int kDmaThreads = 64 * (kDmaProducers + kDmaConsumers);
+constexpr int kXSliceBytes = 16 * 256;                      // 16 rows x 128 k, bf16
+constexpr int kChunkRowBytes = 80;                          // 4 blocks of one row
+constexpr int kChunkBytes = kRowsPerWG * kChunkRowBytes;    // 2560
+constexpr int kSlotBytes = kXSliceBytes + kChunkBytes;      // 6656
+constexpr int kDmaMaxK = 2944;
+constexpr int kDmaMaxChunks = kDmaMaxK / 128;               // 23
+constexpr int kDmaLutCopies = 4;
+
+typedef __attribute__((address_space(3))) volatile uint32_t lds_flag;
+
+__global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t slots[kDmaMaxChunks * kSlotBytes];
+  __shared__ uint32_t lut[256 * kDmaLutCopies];
+  __shared__ uint32_t ready[kDmaMaxChunks];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int r = lane % 16;
+  const int grp = lane / 16;
+  const int kb = g.kb;
+  const int k = 32 * kb;
+  const int chunks = kb / 4;
+  const int n0 = static_cast<int>(blockIdx.x) * kRowsPerWG;
+
+  if (wave >= kDmaConsumers) {
+    // ---------------------------------------------------------- producers
+    const int p = wave - kDmaConsumers;
+    // chunk c into its slot: 4 loads of x (piece q: row q / 16, stored part
+    // q % 16 = global part ^ row; rows past m copy row m - 1), then 3 loads
+    // of weights (piece q: row q / 5, part q % 5; rows past n copy row n - 1).
+    // The copies of other rows only reach outputs that are not stored.
+    auto issue = [&](int c) {
+      uint8_t *dst = slots + c * kSlotBytes;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int piece = 64 * s + lane;
+        const int row = piece >> 4;
+        const int part = (piece & 15) ^ row;
+        const uint16_t *src = g.x + (row < g.m ? row : g.m - 1) * k + 128 * c + 8 * part;
+        __builtin_amdgcn_global_load_lds((const global_void *)src, (lds_void *)(dst + 1024 * s),
+                                         16, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        const int piece = 64 * s + lane;
+        const int row = piece / 5;
+        const int n = n0 + row < g.n ? n0 + row : g.n - 1;
+        const uint8_t *src = g.w + n * kb * 20 + 80 * c + 16 * (piece - 5 * row);
+        if (piece < 5 * kRowsPerWG)
+          __builtin_amdgcn_global_load_lds((const global_void *)src,
+                                           (lds_void *)(dst + kXSliceBytes + 1024 * s), 16, 0, 0);
+      }
+    };
+    const uint32_t flag_addr = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint32_t *)ready));
+    // the first chunk goes out before the barrier that publishes the cleared
+    // flags and the pair table; then up to three chunks stay in flight
+    if (p < chunks) issue(p);
+    __builtin_amdgcn_s_barrier();
+    for (int c = p; c < chunks; c += kDmaProducers) {
+      const bool more1 = c + kDmaProducers < chunks;
+      const bool more2 = c + 2 * kDmaProducers < chunks;
+      if (c == p && more1) issue(c + kDmaProducers);
+      if (more2) issue(c + 2 * kDmaProducers);
+      // loads of chunk c are in once only the later chunks' are outstanding
+      if (more2)
+        __builtin_amdgcn_s_waitcnt(0x0F7E);  // vmcnt(14)
+      else if (more1)
+        __builtin_amdgcn_s_waitcnt(0x0F77);  // vmcnt(7)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      // (written in asm: the compiler cannot tell this flag from the slots
+      // still being filled and would wait for every load in flight first)
+      asm volatile("ds_write_b32 %0, %1" ::"v"(flag_addr + 4 * c), "v"(1u) : "memory");
+    }
+    __syncthreads();  // all chunks consumed
+    __syncthreads();  // partial sums in LDS
+    return;
+  }
+
+  // ------------------------------------------------------------ consumers
+  if (tid < kDmaMaxChunks) ready[tid] = 0u;
+  // pair table: level i sits in lane i; a lane fetches entry e's two levels
+  // with cross-lane reads (no memory access)
+  {
+    float lv = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lv = (lane == i) ? g.cb.c[i] : lv;
+    const int lvb = __builtin_bit_cast(int, lv);
+    for (int i = tid; i < 256 * kDmaLutCopies; i += 64 * kDmaConsumers) {
+      const int e = i / kDmaLutCopies;
+      const float lo = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (e & 15), lvb));
+      const float hi = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (e >> 4), lvb));
+      lut[i] = pack_f16x2(lo, hi);
+    }
+  }
+  bf16x8 h_lo, h_hi;
+  {
+    const int j_lo = 8 * (r >> 2) + (r & 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = 8 * grp + i;
+      const uint32_t sk = (g.sign_bits >> kk) & 1u;
+      const uint32_t n_lo = (__builtin_popcount(j_lo & kk) & 1) ^ sk;
+      const uint32_t n_hi = (__builtin_popcount((j_lo + 4) & kk) & 1) ^ sk;
+      h_lo[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x3F80u | (n_lo << 15)));
+      h_hi[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x3F80u | (n_hi << 15)));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): flags and pair table written
+  __builtin_amdgcn_s_barrier();
+
+  const uint32_t *my_lut = lut + (lane % kDmaLutCopies);
+  const int half = grp >> 1;
+  floatx4 acc[kRowTiles];
+#pragma unroll
+  for (int j = 0; j < kRowTiles; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+  for (int c = wave; c < chunks; c += kDmaConsumers) {
+    while (*(lds_flag *)(&ready[c]) == 0u) __builtin_amdgcn_s_sleep(1);
+    const uint8_t *sl = slots + c * kSlotBytes;
+    half8 a[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 xb8 = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4 *>(sl + 256 * r + 16 * ((4 * t + grp) ^ r)));
+      const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_lo, xb8, zero, 0, 0, 0);
+      const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_hi, xb8, zero, 0, 0, 0);
+      a[t] = __builtin_bit_cast(half8, make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
+                                                  pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])));
+    }
+#pragma unroll
+    for (int j = 0; j < kRowTiles; ++j) {
+      const uint8_t *wr = sl + kXSliceBytes + (16 * j + r) * kChunkRowBytes;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t codes = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 4 * grp);
+        const uint32_t sw = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 16);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            a[t], dequant8<kDmaLutCopies>(codes, half_scale(sw, half), my_lut), acc[j], 0, 0, 0);
+      }
+    }
+  }
+
+  __syncthreads();  // every chunk consumed; partial sums reuse the slots
+  floatx4 *red = reinterpret_cast<floatx4 *>(slots);  // [kDmaConsumers][kRowTiles][64]
+#pragma unroll
+  for (int j = 0; j < kRowTiles; ++j) red[(wave * kRowTiles + j) * 64 + lane] = acc[j];
+  __syncthreads();
+  if (wave < kRowTiles) {
+    floatx4 sum = red[wave * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kDmaConsumers; ++w) sum += red[(w * kRowTiles + wave) * 64 + lane];
+    const int n = n0 + r + 16 * wave;
+    if (n < g.n) {
+      const float rs32 = 0x1.6a09e6p-3f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * grp + v;
+        if (m < g.m) g.y[static_cast<int64_t>(m) * g.n + n] = sum[v] * rs32;
+      }
+    }
+  }
+}
+
 template <int CH, int XL>
 hipError_t launch_cfg(const SkinnyArgs &a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((a.n + kRowsPerWG - 1) / kRowsPerWG);
@@ -321,6 +514,12 @@ hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t 
   a.kb = static_cast<int32_t>(k / 32);
   a.sign_bits = sign_bits;
   a.cb = codebook();
+  if ((k / 32) % 4 == 0 && k <= kDmaMaxK && reinterpret_cast<uintptr_t>(packed) % 16 == 0 &&
+      reinterpret_cast<uintptr_t>(x) % 16 == 0) {
+    const unsigned grid = static_cast<unsigned>((n + kRowsPerWG - 1) / kRowsPerWG);
+    hipLaunchKernelGGL(skinny_dma_kernel, dim3(grid), dim3(kDmaThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const int64_t chunks = (k / 32 + 3) / 4;                          // <= 32
   const int64_t per_wave = (chunks + kConsumers - 1) / kConsumers;  // <= 4
   const int xl = static_cast<int>((k / 8 + 63) / 64);               // <= 8
