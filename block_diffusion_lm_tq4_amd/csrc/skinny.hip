@@ -313,7 +313,7 @@ constexpr int kChunkBytes = kRowsPerWG * kChunkRowBytes;    // 2560
 constexpr int kSlotBytes = kXSliceBytes + kChunkBytes;      // 6656
 constexpr int kDmaMaxK = 2944;
 constexpr int kDmaMaxChunks = kDmaMaxK / 128;               // 23
-constexpr int kDmaLutCopies = 4;
+constexpr int kDmaLutCopies = 8;
 
 typedef __attribute__((address_space(3))) volatile uint32_t lds_flag;
 
@@ -453,23 +453,22 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
   }
 
   __syncthreads();  // every chunk consumed; partial sums reuse the slots
-  floatx4 *red = reinterpret_cast<floatx4 *>(slots);  // [kDmaConsumers][kRowTiles][64]
+  float *red = reinterpret_cast<float *>(slots);  // [kDmaConsumers][kRowTiles][4][64]
 #pragma unroll
-  for (int j = 0; j < kRowTiles; ++j) red[(wave * kRowTiles + j) * 64 + lane] = acc[j];
+  for (int j = 0; j < kRowTiles; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((wave * kRowTiles + j) * 4 + v) * 64 + lane] = acc[j][v];
   __syncthreads();
-  if (wave < kRowTiles) {
-    floatx4 sum = red[wave * 64 + lane];
+  // wave 4 v + j adds up C[4 grp + v][r] of row tile j over the consumers
+  if (wave < 4 * kRowTiles) {
+    const int j = wave % kRowTiles;
+    const int v = wave / kRowTiles;
+    float sum = red[(j * 4 + v) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < kDmaConsumers; ++w) sum += red[(w * kRowTiles + wave) * 64 + lane];
-    const int n = n0 + r + 16 * wave;
-    if (n < g.n) {
-      const float rs32 = 0x1.6a09e6p-3f;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 4 * grp + v;
-        if (m < g.m) g.y[static_cast<int64_t>(m) * g.n + n] = sum[v] * rs32;
-      }
-    }
+    for (int w = 1; w < kDmaConsumers; ++w) sum += red[((w * kRowTiles + j) * 4 + v) * 64 + lane];
+    const int n = n0 + r + 16 * j;
+    const int m = 4 * grp + v;
+    if (n < g.n && m < g.m) g.y[static_cast<int64_t>(m) * g.n + n] = sum * 0x1.6a09e6p-3f;
   }
 }
 
