@@ -307,6 +307,215 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// Dense large-M variant of the same product, software-pipelined by k-step.
+// Tile: 128 activation rows x 256 weight rows per workgroup, 4 waves of
+// 128 x 64 (8 x 4 MFMA tiles, 128 accumulators held in AGPRs for the whole
+// loop).  Within a chunk, while the 32 MFMAs of step t issue, the wave
+// decodes the weight fragments of step t+1 and reads its activation
+// fragments; the last step of a chunk prefetches the first step of the next
+// one, with the chunk's barrier placed after that step's MFMAs are issued.
+// Activation chunks stream into three LDS buffers (LDS-direct loads, as in
+// gemm_kernel) and weight blocks into three register sets, two chunks ahead
+// of the multiply: what bounds this shape is how fast a compute unit takes
+// in its tiles, so the loads in flight matter more than anything else.
+constexpr int kBigMSub = 8;
+constexpr int kBigNSub = 4;
+constexpr int kBigLut = 32;
+constexpr int kBigTM = 16 * kBigMSub;           // 128
+constexpr int kBigTN = 16 * kBigNSub * kWaves;  // 256
+
+__global__ __launch_bounds__(64 * kWaves) void gemm_big_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t abuf0[kBigTM * kChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf1[kBigTM * kChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf2[kBigTM * kChunkBytes];
+  __shared__ uint32_t lut[256 * kBigLut];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int r = lane % 16;
+  const int grp = lane / 16;
+
+  // Workgroup ids go round robin over the 8 XCDs.  XCD x takes a band of
+  // tiles_m / 8 activation tiles and, within it, runs the activation tiles
+  // fastest: the workgroups in flight on one XCD then share a few weight
+  // tiles and a few activation tiles, which its L2 keeps.
+  int mt, nt;
+  {
+    const int id = static_cast<int>(blockIdx.x);
+    if (g.tiles_m % 8 == 0) {
+      const int band = g.tiles_m / 8;
+      const int j = id / 8;
+      mt = (id % 8) * band + j % band;
+      nt = j / band;
+    } else {
+      mt = id / g.tiles_n;
+      nt = id % g.tiles_n;
+    }
+  }
+  const int64_t m_base = static_cast<int64_t>(mt) * kBigTM;
+  const int64_t n_base = static_cast<int64_t>(nt) * kBigTN;
+  const int64_t rows_valid = g.m - m_base;
+
+  for (int i = tid; i < 256 * kBigLut; i += 64 * kWaves) {
+    const int e = i / kBigLut;
+    lut[i] = f16_bits(g.cb.c[e & 15]) | (f16_bits(g.cb.c[e >> 4]) << 16);
+  }
+  const uint32_t *lutp = lut + (lane % kBigLut);
+
+  const int kb = static_cast<int>(g.k / 32);
+  const int chunks = g.chunks;
+
+  const uint16_t *asrc[kBigMSub];
+  int aslot[kBigMSub];
+#pragma unroll
+  for (int i = 0; i < kBigMSub; ++i) {
+    const int row = 4 * (wave * kBigMSub + i) + lane / 16;
+    asrc[i] = g.a + (m_base + (row < rows_valid ? row : 0)) * g.k;
+    aslot[i] = (lane % 16) ^ (row % 16);
+  }
+  auto issue_a = [&](int c, uint8_t *buf) {
+#pragma unroll
+    for (int i = 0; i < kBigMSub; ++i) {
+      const int blk = 4 * c + aslot[i] / 4;
+      const uint16_t *src = asrc[i] + (blk < kb ? 128 * c + 8 * aslot[i] : 0);
+      __builtin_amdgcn_global_load_lds((const global_void *)src,
+                                       (lds_void *)(buf + (wave * kBigMSub + i) * 4 * kChunkBytes),
+                                       16, 0, 0);
+    }
+  };
+  const uint8_t *wrow[kBigNSub];
+  bool w_ok[kBigNSub];
+#pragma unroll
+  for (int j = 0; j < kBigNSub; ++j) {
+    const int64_t n = n_base + wave * (16 * kBigNSub) + 16 * j + r;
+    w_ok[j] = n < g.n;
+    wrow[j] = g.w + (w_ok[j] ? n : 0) * kb * 20;
+  }
+  auto load_w = [&](int c, WRaw (&wr)[kBigNSub]) {
+    const int b = 4 * c + grp;
+    const bool b_ok = b < kb;
+#pragma unroll
+    for (int j = 0; j < kBigNSub; ++j) {
+      const uint32_t *p = reinterpret_cast<const uint32_t *>(wrow[j] + (b_ok ? b : 0) * 20);
+#pragma unroll
+      for (int q = 0; q < 5; ++q) wr[j].v[q] = p[q];
+    }
+  };
+  // scale words of a chunk (zero for blocks past k and rows past n)
+  auto scales = [&](const WRaw (&wr)[kBigNSub], int c, half2v (&sc)[kBigNSub][2]) {
+    const bool b_ok = 4 * c + grp < kb;
+#pragma unroll
+    for (int j = 0; j < kBigNSub; ++j) {
+      const uint32_t sw = (b_ok && w_ok[j]) ? wr[j].v[4] : 0u;
+      sc[j][0] = scale_pair(sw & 0xFFFFu);
+      sc[j][1] = scale_pair(sw >> 16);
+    }
+  };
+  auto decode = [&](const WRaw (&wr)[kBigNSub], const half2v (&sc)[kBigNSub][2], int t,
+                    half8 (&bq)[kBigNSub]) {
+#pragma unroll
+    for (int j = 0; j < kBigNSub; ++j) bq[j] = dequant8<kBigLut>(wr[j].v[t], sc[j][t >> 1], lutp);
+  };
+  auto read_a = [&](const uint8_t *abase, int t, half8 (&aq)[kBigMSub]) {
+    const int slot = (4 * grp + t) ^ r;
+#pragma unroll
+    for (int i = 0; i < kBigMSub; ++i)
+      aq[i] = *reinterpret_cast<const half8 *>(abase + (16 * i + r) * kChunkBytes + 16 * slot);
+  };
+
+  asm volatile("" ::"a"(0));
+  floatx4 acc[kBigMSub][kBigNSub];
+#pragma unroll
+  for (int i = 0; i < kBigMSub; ++i)
+#pragma unroll
+    for (int j = 0; j < kBigNSub; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto mfmas = [&](const half8 (&aq)[kBigMSub], const half8 (&bq)[kBigNSub]) {
+#pragma unroll
+    for (int i = 0; i < kBigMSub; ++i)
+#pragma unroll
+      for (int j = 0; j < kBigNSub; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[i], bq[j], acc[i][j], 0, 0, 0);
+  };
+
+  // One chunk: steps t = 0..3 on (cur, wr); step 0's operands (aq, bq) are
+  // ready on entry, and on exit hold step 0 of the next chunk.  Chunk c + 2
+  // is requested into (far, wf) on entry; chunk c + 1 (nxt, wn) is waited
+  // for at the end.  The chunk count is padded to a multiple of three:
+  // chunks past the end load valid addresses and get zero scales, so every
+  // chunk issues and waits for the same loads and the waits are exact.
+  auto chunk = [&](int c, const uint8_t *cur, uint8_t *nxt, uint8_t *far, WRaw (&wr)[kBigNSub],
+                   WRaw (&wn)[kBigNSub], WRaw (&wf)[kBigNSub], half8 (&aq)[kBigMSub],
+                   half8 (&bq)[kBigNSub]) {
+    issue_a(c + 2, far);
+    load_w(c + 2, wf);
+    half2v sc[kBigNSub][2];
+    scales(wr, c, sc);
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      half8 aq2[kBigMSub], bq2[kBigNSub];
+      decode(wr, sc, t + 1, bq2);
+      read_a(cur, t + 1, aq2);
+      mfmas(aq, bq);
+#pragma unroll
+      for (int i = 0; i < kBigMSub; ++i) aq[i] = aq2[i];
+#pragma unroll
+      for (int j = 0; j < kBigNSub; ++j) bq[j] = bq2[j];
+    }
+    // step 3, and the first step of the next chunk: loads retire in issue
+    // order, so chunk c + 1 is in once only chunk c + 2's 16 loads are
+    // outstanding
+    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+    half8 bq2[kBigNSub];
+    half2v sn[kBigNSub][2];
+    scales(wn, c + 1, sn);
+    decode(wn, sn, 0, bq2);
+    mfmas(aq, bq);
+    // next activation chunk visible (every wave waited for its own loads of
+    // it above); `cur` free again.  A bare barrier: __syncthreads would also
+    // wait for the loads of chunk c + 2.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    read_a(nxt, 0, aq);
+#pragma unroll
+    for (int j = 0; j < kBigNSub; ++j) bq[j] = bq2[j];
+  };
+
+  WRaw w0[kBigNSub], w1[kBigNSub], w2[kBigNSub];
+  half8 aq[kBigMSub], bq[kBigNSub];
+  issue_a(0, abuf0);
+  load_w(0, w0);
+  issue_a(1, abuf1);
+  load_w(1, w1);
+  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): chunk 0 is in
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): pair table written
+  __builtin_amdgcn_s_barrier();        // pair table and the first activation chunk in LDS
+  {
+    half2v sc[kBigNSub][2];
+    scales(w0, 0, sc);
+    decode(w0, sc, 0, bq);
+    read_a(abuf0, 0, aq);
+  }
+  for (int c = 0; c < chunks; c += 3) {
+    chunk(c, abuf0, abuf1, abuf2, w0, w1, w2, aq, bq);
+    chunk(c + 1, abuf1, abuf2, abuf0, w1, w2, w0, aq, bq);
+    chunk(c + 2, abuf2, abuf0, abuf1, w2, w0, w1, aq, bq);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding chunks' loads
+
+#pragma unroll
+  for (int i = 0; i < kBigMSub; ++i)
+#pragma unroll
+    for (int j = 0; j < kBigNSub; ++j) {
+      const int64_t n = n_base + wave * (16 * kBigNSub) + 16 * j + r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = m_base + 16 * i + 4 * grp + v;
+        if (m < g.m && n < g.n) g.out[m * g.n + n] = acc[i][j][v];
+      }
+    }
+}
+
 // y[i] = sum over splits of partial[s][i], in split order.
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ partial,
                                                               int32_t ksplit, int64_t mn,
@@ -336,6 +545,10 @@ hipError_t dispatch(int msub, int nsub, const GemmArgs &g, dim3 grid, hipStream_
     }
   }
   if constexpr (MODE == kDense) {
+    if (nsub == 4 && msub == 8 && g.ksplit == 1) {
+      hipLaunchKernelGGL(gemm_big_kernel, grid, dim3(64 * kWaves), 0, s, g);
+      return hipGetLastError();
+    }
     if (nsub == 4 && msub == 8) return launch_cfg<8, 4, 32, MODE>(g, grid, s);
   }
   return hipErrorInvalidValue;
