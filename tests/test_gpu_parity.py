@@ -139,10 +139,39 @@ def test_linear_dense_m16_full(dev):
     (1, 32, 1), (1, 2688, 8192), (5, 96, 17), (16, 160, 129), (17, 64, 300),
     (33, 2688, 100), (64, 512, 256), (65, 256, 130), (100, 96, 77), (128, 2688, 256),
     (200, 1856, 300), (3, 4096, 64), (16, 8192, 64), (9, 2688, 8200), (16, 4096, 1000),
+    # M <= 16 streaming kernel at its limits, and just past them
+    (16, 2944, 100), (7, 3072, 64), (16, 128, 40), (2, 384, 33),
+    # large-M kernel: chunk counts padded to a multiple of three, ragged M, N, K
+    (300, 512, 520), (129, 96, 33), (256, 2688, 512),
 ])
 def test_linear_ragged_shapes(dev, m, k, n):
     x, p, y = _linear_case(dev, m, k, n, wseed=m * 7 + n)
     _check_close(y, O.linear(x, p, SB), f"linear {m}x{k}x{n}")
+
+
+@pytest.mark.parametrize("offset", [4, 16])
+def test_linear_packed_alignment(dev, offset):
+    """Packed weights 4 bytes past a 16-byte boundary take the register-load
+    M <= 16 kernel; 16 bytes past take the LDS-direct one.  Same results."""
+    m, k, n = 16, 2688, 300
+    w = I.weights(n, k)
+    x = I.activations_bf16(m, k)
+    p = _ops().pack(torch.from_numpy(w).to(dev), SB)
+    flat = torch.zeros(p.numel() + offset, dtype=torch.uint8, device=dev)
+    flat[offset:] = p.reshape(-1)
+    pv = flat[offset:].view(p.shape)
+    assert (pv.data_ptr() % 16 == 0) == (offset == 16)
+    y = _ops().linear(_bf16(x, dev), pv, SB)
+    torch.cuda.synchronize()
+    _check_close(y.cpu().numpy(), O.linear(x, O.pack(w, SB), SB), f"linear packed offset {offset}")
+
+
+def test_linear_rejects_unaligned_activations(dev):
+    from block_diffusion_lm_tq4_amd._lib import TQ4Error
+    flat = torch.zeros(16 * 256 + 1, dtype=torch.bfloat16, device=dev)
+    p = _ops().pack(torch.from_numpy(I.weights(64, 256)).to(dev), SB)
+    with pytest.raises(TQ4Error, match="ALIGN"):
+        _ops().linear(flat[1:].view(16, 256), p, SB)
 
 
 def test_linear_prefill_m4096_sampled_rows(dev):
