@@ -314,20 +314,29 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
 // decodes the weight fragments of step t+1 and reads its activation
 // fragments; the last step of a chunk prefetches the first step of the next
 // one, with the chunk's barrier placed after that step's MFMAs are issued.
-// Activation chunks stream into three LDS buffers (LDS-direct loads, as in
-// gemm_kernel) and weight blocks into three register sets, two chunks ahead
-// of the multiply: what bounds this shape is how fast a compute unit takes
-// in its tiles, so the loads in flight matter more than anything else.
+//
+// What bounds this shape is how fast a compute unit takes in its tiles, so
+// both operands stream in with LDS-direct loads (1 KB of consecutive memory
+// per instruction), two chunks ahead of the multiply, into three stages:
+// activation chunks (128 rows x 256 bytes, XOR-swizzled) and weight chunks
+// (each wave's 64 rows x 80 bytes).  A wave reads its lanes' 20-byte blocks
+// back from LDS at the start of each chunk.  Requires K to be a multiple of
+// 128 (weight rows 16-byte aligned); other K use gemm_kernel.
 constexpr int kBigMSub = 8;
 constexpr int kBigNSub = 4;
-constexpr int kBigLut = 32;
-constexpr int kBigTM = 16 * kBigMSub;           // 128
-constexpr int kBigTN = 16 * kBigNSub * kWaves;  // 256
+constexpr int kBigLut = 4;
+constexpr int kBigTM = 16 * kBigMSub;                 // 128
+constexpr int kBigTN = 16 * kBigNSub * kWaves;        // 256
+constexpr int kBigWWave = 16 * kBigNSub * 80;         // 5120: a wave's weight chunk
+constexpr int kBigLoads = kBigMSub + kBigWWave / 1024;  // 13 per chunk per wave
 
 __global__ __launch_bounds__(64 * kWaves) void gemm_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t abuf0[kBigTM * kChunkBytes];
   __shared__ __attribute__((aligned(16))) uint8_t abuf1[kBigTM * kChunkBytes];
   __shared__ __attribute__((aligned(16))) uint8_t abuf2[kBigTM * kChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf0[kWaves * kBigWWave];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf1[kWaves * kBigWWave];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf2[kWaves * kBigWWave];
   __shared__ uint32_t lut[256 * kBigLut];
 
   const int tid = threadIdx.x;
@@ -364,8 +373,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_big_kernel(GemmArgs g) {
   const uint32_t *lutp = lut + (lane % kBigLut);
 
   const int kb = static_cast<int>(g.k / 32);
-  const int chunks = g.chunks;
+  const int chunks = g.chunks;  // kb / 4
 
+  // activation rows this lane copies: load i of wave w fills LDS rows
+  // 4 (w kBigMSub + i) + lane / 16, slot lane % 16 = global slot ^ (row % 16)
   const uint16_t *asrc[kBigMSub];
   int aslot[kBigMSub];
 #pragma unroll
@@ -374,40 +385,49 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_big_kernel(GemmArgs g) {
     asrc[i] = g.a + (m_base + (row < rows_valid ? row : 0)) * g.k;
     aslot[i] = (lane % 16) ^ (row % 16);
   }
-  auto issue_a = [&](int c, uint8_t *buf) {
+  // weight pieces this lane copies: load s of the wave takes piece
+  // q = 64 s + lane of its 64 rows x 80 bytes (row q / 5, part q % 5); rows
+  // past n copy row n - 1 and get zero scales
+  const uint8_t *wsrc[kBigWWave / 1024];
 #pragma unroll
-    for (int i = 0; i < kBigMSub; ++i) {
-      const int blk = 4 * c + aslot[i] / 4;
-      const uint16_t *src = asrc[i] + (blk < kb ? 128 * c + 8 * aslot[i] : 0);
-      __builtin_amdgcn_global_load_lds((const global_void *)src,
-                                       (lds_void *)(buf + (wave * kBigMSub + i) * 4 * kChunkBytes),
-                                       16, 0, 0);
-    }
-  };
-  const uint8_t *wrow[kBigNSub];
-  bool w_ok[kBigNSub];
-#pragma unroll
-  for (int j = 0; j < kBigNSub; ++j) {
-    const int64_t n = n_base + wave * (16 * kBigNSub) + 16 * j + r;
-    w_ok[j] = n < g.n;
-    wrow[j] = g.w + (w_ok[j] ? n : 0) * kb * 20;
+  for (int s = 0; s < kBigWWave / 1024; ++s) {
+    const int q = 64 * s + lane;
+    const int row = q / 5;
+    const int64_t n = n_base + wave * (16 * kBigNSub) + row;
+    wsrc[s] = g.w + (n < g.n ? n : g.n - 1) * kb * 20 + 16 * (q - 5 * row);
   }
-  auto load_w = [&](int c, WRaw (&wr)[kBigNSub]) {
-    const int b = 4 * c + grp;
-    const bool b_ok = b < kb;
+  uint32_t w_okm = 0;
+#pragma unroll
+  for (int j = 0; j < kBigNSub; ++j)
+    w_okm |= static_cast<uint32_t>(n_base + wave * (16 * kBigNSub) + 16 * j + r < g.n) << j;
+  // chunk c into stage (abuf, wbuf); chunks past the end (padding, see
+  // below) load the last chunk again and get zero scales
+  auto issue = [&](int c, uint8_t *abuf, uint8_t *wbuf) {
+    const int cc = c < chunks ? c : chunks - 1;
+#pragma unroll
+    for (int i = 0; i < kBigMSub; ++i)
+      __builtin_amdgcn_global_load_lds((const global_void *)(asrc[i] + 128 * cc + 8 * aslot[i]),
+                                       (lds_void *)(abuf + (wave * kBigMSub + i) * 4 * kChunkBytes),
+                                       16, 0, 0);
+#pragma unroll
+    for (int s = 0; s < kBigWWave / 1024; ++s)
+      __builtin_amdgcn_global_load_lds((const global_void *)(wsrc[s] + 80 * cc),
+                                       (lds_void *)(wbuf + wave * kBigWWave + 1024 * s), 16, 0, 0);
+  };
+  // this lane's block 4c + grp of each of its weight rows, from LDS
+  auto read_w = [&](const uint8_t *wbuf, WRaw (&wr)[kBigNSub]) {
 #pragma unroll
     for (int j = 0; j < kBigNSub; ++j) {
-      const uint32_t *p = reinterpret_cast<const uint32_t *>(wrow[j] + (b_ok ? b : 0) * 20);
+      const uint32_t *p =
+          reinterpret_cast<const uint32_t *>(wbuf + wave * kBigWWave + (16 * j + r) * 80 + 20 * grp);
 #pragma unroll
       for (int q = 0; q < 5; ++q) wr[j].v[q] = p[q];
     }
   };
-  // scale words of a chunk (zero for blocks past k and rows past n)
   auto scales = [&](const WRaw (&wr)[kBigNSub], int c, half2v (&sc)[kBigNSub][2]) {
-    const bool b_ok = 4 * c + grp < kb;
 #pragma unroll
     for (int j = 0; j < kBigNSub; ++j) {
-      const uint32_t sw = (b_ok && w_ok[j]) ? wr[j].v[4] : 0u;
+      const uint32_t sw = (c < chunks && ((w_okm >> j) & 1u)) ? wr[j].v[4] : 0u;
       sc[j][0] = scale_pair(sw & 0xFFFFu);
       sc[j][1] = scale_pair(sw >> 16);
     }
@@ -438,68 +458,62 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_big_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[i], bq[j], acc[i][j], 0, 0, 0);
   };
 
+  constexpr int kWaitNext = 0x0F70 | (kBigLoads & 15) | ((kBigLoads >> 4) << 14);  // vmcnt(13)
   // One chunk: steps t = 0..3 on (cur, wr); step 0's operands (aq, bq) are
   // ready on entry, and on exit hold step 0 of the next chunk.  Chunk c + 2
-  // is requested into (far, wf) on entry; chunk c + 1 (nxt, wn) is waited
-  // for at the end.  The chunk count is padded to a multiple of three:
-  // chunks past the end load valid addresses and get zero scales, so every
+  // is requested into the far stage on entry; chunk c + 1 is waited for at
+  // the end.  The chunk count is padded to a multiple of three so that every
   // chunk issues and waits for the same loads and the waits are exact.
-  auto chunk = [&](int c, const uint8_t *cur, uint8_t *nxt, uint8_t *far, WRaw (&wr)[kBigNSub],
-                   WRaw (&wn)[kBigNSub], WRaw (&wf)[kBigNSub], half8 (&aq)[kBigMSub],
-                   half8 (&bq)[kBigNSub]) {
-    issue_a(c + 2, far);
-    load_w(c + 2, wf);
+  auto chunk = [&](int c, const uint8_t *acur, const uint8_t *anxt, uint8_t *afar,
+                   const uint8_t *wnxt, uint8_t *wfar, WRaw (&wr)[kBigNSub],
+                   half8 (&aq)[kBigMSub], half8 (&bq)[kBigNSub]) {
+    issue(c + 2, afar, wfar);
     half2v sc[kBigNSub][2];
     scales(wr, c, sc);
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       half8 aq2[kBigMSub], bq2[kBigNSub];
       decode(wr, sc, t + 1, bq2);
-      read_a(cur, t + 1, aq2);
+      read_a(acur, t + 1, aq2);
       mfmas(aq, bq);
 #pragma unroll
       for (int i = 0; i < kBigMSub; ++i) aq[i] = aq2[i];
 #pragma unroll
       for (int j = 0; j < kBigNSub; ++j) bq[j] = bq2[j];
     }
-    // step 3, and the first step of the next chunk: loads retire in issue
-    // order, so chunk c + 1 is in once only chunk c + 2's 16 loads are
-    // outstanding
-    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
-    half8 bq2[kBigNSub];
-    half2v sn[kBigNSub][2];
-    scales(wn, c + 1, sn);
-    decode(wn, sn, 0, bq2);
+    // step 3; chunk c + 1 is in once only chunk c + 2's loads are
+    // outstanding (loads retire in issue order)
+    __builtin_amdgcn_s_waitcnt(kWaitNext);
     mfmas(aq, bq);
-    // next activation chunk visible (every wave waited for its own loads of
-    // it above); `cur` free again.  A bare barrier: __syncthreads would also
-    // wait for the loads of chunk c + 2.
+    // chunk c + 1 visible to all waves; the current stage free again.  A bare
+    // barrier: __syncthreads would also wait for the loads of chunk c + 2.
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    read_a(nxt, 0, aq);
-#pragma unroll
-    for (int j = 0; j < kBigNSub; ++j) bq[j] = bq2[j];
+    read_w(wnxt, wr);
+    half2v sn[kBigNSub][2];
+    scales(wr, c + 1, sn);
+    decode(wr, sn, 0, bq);
+    read_a(anxt, 0, aq);
   };
 
-  WRaw w0[kBigNSub], w1[kBigNSub], w2[kBigNSub];
+  WRaw wr[kBigNSub];
   half8 aq[kBigMSub], bq[kBigNSub];
-  issue_a(0, abuf0);
-  load_w(0, w0);
-  issue_a(1, abuf1);
-  load_w(1, w1);
-  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): chunk 0 is in
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): pair table written
-  __builtin_amdgcn_s_barrier();        // pair table and the first activation chunk in LDS
+  issue(0, abuf0, wbuf0);
+  issue(1, abuf1, wbuf1);
+  __builtin_amdgcn_s_waitcnt(kWaitNext);  // chunk 0 is in
+  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): pair table written
+  __builtin_amdgcn_s_barrier();
   {
+    read_w(wbuf0, wr);
     half2v sc[kBigNSub][2];
-    scales(w0, 0, sc);
-    decode(w0, sc, 0, bq);
+    scales(wr, 0, sc);
+    decode(wr, sc, 0, bq);
     read_a(abuf0, 0, aq);
   }
   for (int c = 0; c < chunks; c += 3) {
-    chunk(c, abuf0, abuf1, abuf2, w0, w1, w2, aq, bq);
-    chunk(c + 1, abuf1, abuf2, abuf0, w1, w2, w0, aq, bq);
-    chunk(c + 2, abuf2, abuf0, abuf1, w2, w0, w1, aq, bq);
+    chunk(c, abuf0, abuf1, abuf2, wbuf1, wbuf2, wr, aq, bq);
+    chunk(c + 1, abuf1, abuf2, abuf0, wbuf2, wbuf0, wr, aq, bq);
+    chunk(c + 2, abuf2, abuf0, abuf1, wbuf0, wbuf1, wr, aq, bq);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding chunks' loads
 
@@ -545,7 +559,8 @@ hipError_t dispatch(int msub, int nsub, const GemmArgs &g, dim3 grid, hipStream_
     }
   }
   if constexpr (MODE == kDense) {
-    if (nsub == 4 && msub == 8 && g.ksplit == 1) {
+    if (nsub == 4 && msub == 8 && g.ksplit == 1 && g.k % 128 == 0 &&
+        reinterpret_cast<uintptr_t>(g.w) % 16 == 0) {
       hipLaunchKernelGGL(gemm_big_kernel, grid, dim3(64 * kWaves), 0, s, g);
       return hipGetLastError();
     }
