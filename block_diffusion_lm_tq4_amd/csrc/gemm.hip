@@ -530,6 +530,194 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_big_kernel(GemmArgs g) {
     }
 }
 
+// Dense large-M variant with two waves on every SIMD.  Tile: 256 activation
+// rows x 256 weight rows per workgroup, 8 waves of 128 x 64 (2 along m, 4
+// along n; 8 x 4 MFMA tiles, 128 accumulators each, so a wave fits in half a
+// SIMD's registers and the other wave's decode and LDS reads overlap its
+// MFMAs).  Chunks are 64 k (2 blocks): activation chunks are 256 rows x 128
+// bytes (16-byte pieces XOR-swizzled by row % 8), weight chunks 256 rows x
+// 40 bytes, both streamed in with LDS-direct loads two chunks ahead into
+// three stages.  Activation pieces move 16 bytes per lane; weight rows of 40
+// bytes move as dwords, so packed weights need only 4-byte alignment.
+//
+// k-slots: lane group g = 2b + h takes block b of the chunk, elements
+// 16h + 8t .. 16h + 8t + 7 at step t in 0..1 (codes word 2h + t, half-block
+// scale h); the activation side reads k = 16g + 8t of the chunk to match.
+// Requires K to be a multiple of 64.
+constexpr int kHugeWaves = 8;
+constexpr int kHugeMSub = 8;
+constexpr int kHugeNSub = 4;
+constexpr int kHugeLut = 32;
+constexpr int kHugeTM = 2 * 16 * kHugeMSub;                    // 256
+constexpr int kHugeTN = (kHugeWaves / 2) * 16 * kHugeNSub;     // 256
+constexpr int kHugeRowA = 128;                                 // 64 k of fp16
+constexpr int kHugeRowW = 40;                                  // 2 blocks
+constexpr int kHugeALoads = kHugeTM * kHugeRowA / 1024 / kHugeWaves;  // 4
+constexpr int kHugeWLoads = kHugeTN * kHugeRowW / 256 / kHugeWaves;   // 5
+constexpr int kHugeLoads = kHugeALoads + kHugeWLoads;                 // 9
+
+__global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t abuf0[kHugeTM * kHugeRowA];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf1[kHugeTM * kHugeRowA];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf2[kHugeTM * kHugeRowA];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf0[kHugeTN * kHugeRowW];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf1[kHugeTN * kHugeRowW];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf2[kHugeTN * kHugeRowW];
+  __shared__ uint32_t lut[256 * kHugeLut];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int r = lane % 16;
+  const int grp = lane / 16;
+  const int wm = wave / (kHugeWaves / 2);
+  const int wn = wave % (kHugeWaves / 2);
+
+  // XCD-banded tile order, as in gemm_big_kernel
+  int mt, nt;
+  {
+    const int id = static_cast<int>(blockIdx.x);
+    if (g.tiles_m % 8 == 0) {
+      const int band = g.tiles_m / 8;
+      const int j = id / 8;
+      mt = (id % 8) * band + j % band;
+      nt = j / band;
+    } else {
+      mt = id / g.tiles_n;
+      nt = id % g.tiles_n;
+    }
+  }
+  const int64_t m_base = static_cast<int64_t>(mt) * kHugeTM;
+  const int64_t n_base = static_cast<int64_t>(nt) * kHugeTN;
+  const int64_t rows_valid = g.m - m_base;
+
+  for (int i = tid; i < 256 * kHugeLut; i += 64 * kHugeWaves) {
+    const int e = i / kHugeLut;
+    lut[i] = f16_bits(g.cb.c[e & 15]) | (f16_bits(g.cb.c[e >> 4]) << 16);
+  }
+  const uint32_t *lutp = lut + (lane % kHugeLut);
+
+  const int kb = static_cast<int>(g.k / 32);
+  const int chunks = kb / 2;
+
+  // Source offsets (bytes, from the tile's first row; 32-bit, loop
+  // invariant) of what this lane copies.  Activation piece
+  // p = kHugeALoads * wave + i holds rows 8p .. 8p + 7: lane l fills row
+  // 8p + l / 8, slot l % 8 with global piece slot ^ (row % 8).
+  const uint8_t *a_tile = reinterpret_cast<const uint8_t *>(g.a + m_base * g.k);
+  uint32_t aoff[kHugeALoads];
+#pragma unroll
+  for (int i = 0; i < kHugeALoads; ++i) {
+    const int row = 8 * (kHugeALoads * wave + i) + lane / 8;
+    aoff[i] = static_cast<uint32_t>((row < rows_valid ? row : 0) * g.k * 2) +
+              16u * static_cast<uint32_t>((lane % 8) ^ (row % 8));
+  }
+  // Weight piece p = kHugeWLoads * wave + s is bytes 256p .. 256p + 255 of
+  // the chunk's 256 rows x 40 bytes; rows past n copy row n - 1 and get zero
+  // scales.
+  const uint8_t *w_tile = g.w + n_base * kb * 20;
+  uint32_t woff[kHugeWLoads];
+#pragma unroll
+  for (int s = 0; s < kHugeWLoads; ++s) {
+    const int o = 256 * (kHugeWLoads * wave + s) + 4 * lane;
+    const int row = o / kHugeRowW;
+    const int64_t nrow = n_base + row < g.n ? row : g.n - 1 - n_base;
+    woff[s] = static_cast<uint32_t>(nrow * kb * 20 + (o - kHugeRowW * row));
+  }
+  uint32_t w_okm = 0;
+#pragma unroll
+  for (int j = 0; j < kHugeNSub; ++j)
+    w_okm |= static_cast<uint32_t>(n_base + wn * (16 * kHugeNSub) + 16 * j + r < g.n) << j;
+  auto issue = [&](int c, uint8_t *abuf, uint8_t *wbuf) __attribute__((always_inline)) {
+    const int cc = c < chunks ? c : chunks - 1;
+    const uint8_t *ac = a_tile + kHugeRowA * cc;
+    const uint8_t *wc = w_tile + kHugeRowW * cc;
+#pragma unroll
+    for (int i = 0; i < kHugeALoads; ++i)
+      __builtin_amdgcn_global_load_lds((const global_void *)(ac + aoff[i]),
+                                       (lds_void *)(abuf + (kHugeALoads * wave + i) * 1024), 16,
+                                       0, 0);
+#pragma unroll
+    for (int s = 0; s < kHugeWLoads; ++s)
+      __builtin_amdgcn_global_load_lds((const global_void *)(wc + woff[s]),
+                                       (lds_void *)(wbuf + (kHugeWLoads * wave + s) * 256), 4, 0,
+                                       0);
+  };
+
+  floatx4 acc[kHugeMSub][kHugeNSub];
+#pragma unroll
+  for (int i = 0; i < kHugeMSub; ++i)
+#pragma unroll
+    for (int j = 0; j < kHugeNSub; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int blk = grp >> 1;
+  const int half = grp & 1;
+  auto compute = [&](int c, const uint8_t *abuf, const uint8_t *wbuf)
+                     __attribute__((always_inline)) {
+    uint32_t cw[kHugeNSub][2];
+    half2v sc[kHugeNSub];
+#pragma unroll
+    for (int j = 0; j < kHugeNSub; ++j) {
+      const uint32_t *p = reinterpret_cast<const uint32_t *>(
+          wbuf + (wn * (16 * kHugeNSub) + 16 * j + r) * kHugeRowW + 20 * blk);
+      cw[j][0] = p[2 * half];
+      cw[j][1] = p[2 * half + 1];
+      const uint32_t sw = (c < chunks && ((w_okm >> j) & 1u)) ? p[4] : 0u;
+      sc[j] = scale_pair(half ? (sw >> 16) : (sw & 0xFFFFu));
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      half8 bq[kHugeNSub];
+#pragma unroll
+      for (int j = 0; j < kHugeNSub; ++j) bq[j] = dequant8<kHugeLut>(cw[j][t], sc[j], lutp);
+      const int slot = (2 * grp + t) ^ (r % 8);
+#pragma unroll
+      for (int i = 0; i < kHugeMSub; ++i) {
+        const half8 aq = *reinterpret_cast<const half8 *>(
+            abuf + (wm * (16 * kHugeMSub) + 16 * i + r) * kHugeRowA + 16 * slot);
+#pragma unroll
+        for (int j = 0; j < kHugeNSub; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, bq[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  // Chunk c: wait until only chunk c + 1's loads are outstanding (loads
+  // retire in issue order), publish chunk c with a bare barrier (which also
+  // shows that every wave is done with chunk c - 1's stage), refill that
+  // stage with chunk c + 2, multiply chunk c.  The chunk count is padded to
+  // a multiple of three; padding chunks reload the last chunk, get zero
+  // scales, and keep every wait exact.
+  constexpr int kWait = 0x0F70 | (kHugeLoads & 15) | ((kHugeLoads >> 4) << 14);
+  auto step = [&](int c, const uint8_t *acur, const uint8_t *wcur, uint8_t *afar, uint8_t *wfar)
+                  __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kWait);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    issue(c + 2, afar, wfar);
+    compute(c, acur, wcur);
+  };
+  issue(0, abuf0, wbuf0);
+  issue(1, abuf1, wbuf1);
+  for (int c = 0; c < chunks; c += 3) {
+    step(c, abuf0, wbuf0, abuf2, wbuf2);
+    step(c + 1, abuf1, wbuf1, abuf0, wbuf0);
+    step(c + 2, abuf2, wbuf2, abuf1, wbuf1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding chunks' loads
+
+#pragma unroll
+  for (int i = 0; i < kHugeMSub; ++i)
+#pragma unroll
+    for (int j = 0; j < kHugeNSub; ++j) {
+      const int64_t n = n_base + wn * (16 * kHugeNSub) + 16 * j + r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = m_base + wm * (16 * kHugeMSub) + 16 * i + 4 * grp + v;
+        if (m < g.m && n < g.n) g.out[m * g.n + n] = acc[i][j][v];
+      }
+    }
+}
+
 // y[i] = sum over splits of partial[s][i], in split order.
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ partial,
                                                               int32_t ksplit, int64_t mn,
@@ -548,8 +736,9 @@ hipError_t launch_cfg(const GemmArgs &g, dim3 grid, hipStream_t s) {
 }
 
 template <int MODE>
-hipError_t dispatch(int msub, int nsub, const GemmArgs &g, dim3 grid, hipStream_t s) {
-  if (nsub == 2) {
+hipError_t dispatch(int msub, int nsub, int waves_m, const GemmArgs &g, dim3 grid,
+                    hipStream_t s) {
+  if (nsub == 2 && waves_m == 1) {
     switch (msub) {
       case 1: return launch_cfg<1, 2, 8, MODE>(g, grid, s);
       case 2: return launch_cfg<2, 2, 8, MODE>(g, grid, s);
@@ -559,6 +748,11 @@ hipError_t dispatch(int msub, int nsub, const GemmArgs &g, dim3 grid, hipStream_
     }
   }
   if constexpr (MODE == kDense) {
+    if (waves_m == 2 && nsub == 4 && msub == 8 && g.ksplit == 1 && g.k % 64 == 0) {
+      hipLaunchKernelGGL(gemm_huge_kernel, grid, dim3(64 * kHugeWaves), 0, s, g);
+      return hipGetLastError();
+    }
+    if (waves_m != 1) return hipErrorInvalidValue;
     if (nsub == 4 && msub == 8 && g.ksplit == 1 && g.k % 128 == 0 &&
         reinterpret_cast<uintptr_t>(g.w) % 16 == 0) {
       hipLaunchKernelGGL(gemm_big_kernel, grid, dim3(64 * kWaves), 0, s, g);
@@ -583,6 +777,12 @@ DensePlan plan_dense(int64_t m, int64_t k, int64_t n) {
   } else {
     p.msub = 8;
     p.nsub = 4;
+    // 256 x 256 tiles (two waves per SIMD) once there are enough of them to
+    // give every compute unit one; else 128 x 256
+    const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+    if (k % 64 == 0 && tiles256 >= 256 && 256 * k * 2 < (int64_t{1} << 31) &&
+        n * (k / 32) * 20 < (int64_t{1} << 31))
+      p.waves_m = 2;
   }
   const int64_t wg_m = 16 * p.msub * p.waves_m;
   const int64_t wg_n = 16 * p.nsub * p.waves_n;
@@ -618,7 +818,7 @@ hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64
   g.tiles_n = static_cast<int32_t>(p.n_tiles);
   g.cb = codebook();
   const dim3 grid(static_cast<unsigned>(p.n_tiles * p.m_tiles), 1, static_cast<unsigned>(p.ksplit));
-  hipError_t e = dispatch<kDense>(p.msub, p.nsub, g, grid, s);
+  hipError_t e = dispatch<kDense>(p.msub, p.nsub, p.waves_m, g, grid, s);
   if (e != hipSuccess || p.ksplit == 1) return e;
   const int64_t mn = m * n;
   hipLaunchKernelGGL(reduce_partials_kernel, dim3(static_cast<unsigned>((mn + 255) / 256)),
@@ -660,8 +860,8 @@ hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_
   const int64_t wg_n = 16 * p.nsub * p.waves_n;
   const dim3 grid(static_cast<unsigned>((n + wg_n - 1) / wg_n), static_cast<unsigned>(p.max_tiles),
                   1);
-  if (mode == 0) return dispatch<kMoEUp>(p.msub, p.nsub, g, grid, s);
-  return dispatch<kMoEDown>(p.msub, p.nsub, g, grid, s);
+  if (mode == 0) return dispatch<kMoEUp>(p.msub, p.nsub, p.waves_m, g, grid, s);
+  return dispatch<kMoEDown>(p.msub, p.nsub, p.waves_m, g, grid, s);
 }
 
 }  // namespace tq4

@@ -143,6 +143,9 @@ def test_linear_dense_m16_full(dev):
     (16, 2944, 100), (7, 3072, 64), (16, 128, 40), (2, 384, 33),
     # large-M kernel: chunk counts padded to a multiple of three, ragged M, N, K
     (300, 512, 520), (129, 96, 33), (256, 2688, 512),
+    # 256 x 256 tiles (256 or more of them): K = 64 * (5, 2, 3) chunks (padding
+    # of 1, 1, 0), one valid row or column in the last tile
+    (257, 320, 32761), (512, 128, 32768), (300, 192, 32769),
 ])
 def test_linear_ragged_shapes(dev, m, k, n):
     x, p, y = _linear_case(dev, m, k, n, wseed=m * 7 + n)
