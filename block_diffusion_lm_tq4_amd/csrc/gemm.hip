@@ -555,6 +555,8 @@ constexpr int kHugeRowW = 40;                                  // 2 blocks
 constexpr int kHugeALoads = kHugeTM * kHugeRowA / 1024 / kHugeWaves;  // 4
 constexpr int kHugeWLoads = kHugeTN * kHugeRowW / 256 / kHugeWaves;   // 5
 constexpr int kHugeLoads = kHugeALoads + kHugeWLoads;                 // 9
+// buffer resource word 3 for raw (untyped) dword loads on gfx9-family parts
+constexpr int kBufferFlags = 0x00020000;
 
 __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t abuf0[kHugeTM * kHugeRowA];
@@ -566,7 +568,7 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
   __shared__ uint32_t lut[256 * kHugeLut];
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64;
   const int r = lane % 16;
   const int grp = lane / 16;
@@ -600,11 +602,14 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
   const int kb = static_cast<int>(g.k / 32);
   const int chunks = kb / 2;
 
-  // Source offsets (bytes, from the tile's first row; 32-bit, loop
-  // invariant) of what this lane copies.  Activation piece
+  // Loads go through buffer resources over the workgroup's activation and
+  // weight rows: the per-lane source offsets (bytes, 32-bit) are loop
+  // invariant and the chunk's offset is a scalar.  Activation piece
   // p = kHugeALoads * wave + i holds rows 8p .. 8p + 7: lane l fills row
   // 8p + l / 8, slot l % 8 with global piece slot ^ (row % 8).
-  const uint8_t *a_tile = reinterpret_cast<const uint8_t *>(g.a + m_base * g.k);
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(g.a + m_base * g.k), static_cast<short>(0),
+      static_cast<int>(kHugeTM * g.k * 2), kBufferFlags);
   uint32_t aoff[kHugeALoads];
 #pragma unroll
   for (int i = 0; i < kHugeALoads; ++i) {
@@ -615,7 +620,9 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
   // Weight piece p = kHugeWLoads * wave + s is bytes 256p .. 256p + 255 of
   // the chunk's 256 rows x 40 bytes; rows past n copy row n - 1 and get zero
   // scales.
-  const uint8_t *w_tile = g.w + n_base * kb * 20;
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.w + n_base * kb * 20), static_cast<short>(0),
+      static_cast<int>(kHugeTN * kb * 20), kBufferFlags);
   uint32_t woff[kHugeWLoads];
 #pragma unroll
   for (int s = 0; s < kHugeWLoads; ++s) {
@@ -630,18 +637,16 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
     w_okm |= static_cast<uint32_t>(n_base + wn * (16 * kHugeNSub) + 16 * j + r < g.n) << j;
   auto issue = [&](int c, uint8_t *abuf, uint8_t *wbuf) __attribute__((always_inline)) {
     const int cc = c < chunks ? c : chunks - 1;
-    const uint8_t *ac = a_tile + kHugeRowA * cc;
-    const uint8_t *wc = w_tile + kHugeRowW * cc;
 #pragma unroll
     for (int i = 0; i < kHugeALoads; ++i)
-      __builtin_amdgcn_global_load_lds((const global_void *)(ac + aoff[i]),
-                                       (lds_void *)(abuf + (kHugeALoads * wave + i) * 1024), 16,
-                                       0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          a_rsrc, (lds_void *)(abuf + (kHugeALoads * wave + i) * 1024), 16, aoff[i],
+          kHugeRowA * cc, 0, 0);
 #pragma unroll
     for (int s = 0; s < kHugeWLoads; ++s)
-      __builtin_amdgcn_global_load_lds((const global_void *)(wc + woff[s]),
-                                       (lds_void *)(wbuf + (kHugeWLoads * wave + s) * 256), 4, 0,
-                                       0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rsrc, (lds_void *)(wbuf + (kHugeWLoads * wave + s) * 256), 4, woff[s],
+          kHugeRowW * cc, 0, 0);
   };
 
   floatx4 acc[kHugeMSub][kHugeNSub];
