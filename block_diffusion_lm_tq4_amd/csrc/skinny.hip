@@ -426,30 +426,62 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
 #pragma unroll
   for (int j = 0; j < kRowTiles; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+  // A chunk is processed in phases, so that its LDS accesses form two
+  // batches (the chunk's words, then the table lookups they index) instead
+  // of one round trip per block: what bounds a consumer is LDS latency, and
+  // the last chunk's latency is the kernel's tail.
   for (int c = wave; c < chunks; c += kDmaConsumers) {
     while (*(lds_flag *)(&ready[c]) == 0u) __builtin_amdgcn_s_sleep(1);
     const uint8_t *sl = slots + c * kSlotBytes;
-    half8 a[4];
+    // 1. this lane's x parts, code words and half-block scales
+    bf16x8 xb[4];
+    uint32_t cw[kRowTiles][4], sc[kRowTiles][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bf16x8 xb8 = __builtin_bit_cast(
+    for (int t = 0; t < 4; ++t)
+      xb[t] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const uint4 *>(sl + 256 * r + 16 * ((4 * t + grp) ^ r)));
-      const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_lo, xb8, zero, 0, 0, 0);
-      const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_hi, xb8, zero, 0, 0, 0);
-      a[t] = __builtin_bit_cast(half8, make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
-                                                  pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])));
-    }
 #pragma unroll
     for (int j = 0; j < kRowTiles; ++j) {
       const uint8_t *wr = sl + kXSliceBytes + (16 * j + r) * kChunkRowBytes;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const uint32_t codes = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 4 * grp);
-        const uint32_t sw = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 16);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            a[t], dequant8<kDmaLutCopies>(codes, half_scale(sw, half), my_lut), acc[j], 0, 0, 0);
+        cw[j][t] = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 4 * grp);
+        sc[j][t] = *reinterpret_cast<const uint16_t *>(wr + 20 * t + 16 + 2 * half);
       }
     }
+    // 2. every level pair the chunk's codes select
+    uint32_t pr[kRowTiles][4][4];
+#pragma unroll
+    for (int j = 0; j < kRowTiles; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          pr[j][t][b] = my_lut[((cw[j][t] >> (8 * b)) & 0xFFu) * kDmaLutCopies];
+    // 3. rotated activations of the chunk's 4 blocks
+    half8 a[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_lo, xb[t], zero, 0, 0, 0);
+      const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_hi, xb[t], zero, 0, 0, 0);
+      a[t] = __builtin_bit_cast(half8, make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
+                                                  pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])));
+    }
+    // 4. scale the pairs and accumulate
+#pragma unroll
+    for (int j = 0; j < kRowTiles; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const half2v s = scale_pair(sc[j][t]);
+        half8 bq;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const half2v p = __builtin_bit_cast(half2v, pr[j][t][b]) * s;
+          bq[2 * b] = p[0];
+          bq[2 * b + 1] = p[1];
+        }
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bq, acc[j], 0, 0, 0);
+      }
   }
 
   __syncthreads();  // every chunk consumed; partial sums reuse the slots
