@@ -535,7 +535,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_big_kernel(GemmArgs g) {
 // along n; 8 x 4 MFMA tiles, 128 accumulators each, so a wave fits in half a
 // SIMD's registers and the other wave's decode and LDS reads overlap its
 // MFMAs).  Chunks are 64 k (2 blocks): activation chunks are 256 rows x 128
-// bytes (16-byte pieces XOR-swizzled by row % 8), weight chunks 256 rows x
+// bytes (16-byte pieces XOR-swizzled by (row / 2) % 8), weight chunks 256 rows x
 // 40 bytes, both streamed in with LDS-direct loads two chunks ahead into
 // three stages.  Activation pieces move 16 bytes per lane; weight rows of 40
 // bytes move as dwords, so packed weights need only 4-byte alignment.
@@ -606,7 +606,10 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
   // weight rows: the per-lane source offsets (bytes, 32-bit) are loop
   // invariant and the chunk's offset is a scalar.  Activation piece
   // p = kHugeALoads * wave + i holds rows 8p .. 8p + 7: lane l fills row
-  // 8p + l / 8, slot l % 8 with global piece slot ^ (row % 8).
+  // 8p + l / 8, slot l % 8 with global piece slot ^ ((row / 2) % 8).  The LDS
+  // has 64 four-byte banks, so a 128-byte row covers half of them: the 16
+  // rows of a fragment read hit distinct 16-byte bank groups when the key
+  // differs between rows of equal parity.
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(g.a + m_base * g.k), static_cast<short>(0),
       static_cast<int>(kHugeTM * g.k * 2), kBufferFlags);
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
   for (int i = 0; i < kHugeALoads; ++i) {
     const int row = 8 * (kHugeALoads * wave + i) + lane / 8;
     aoff[i] = static_cast<uint32_t>((row < rows_valid ? row : 0) * g.k * 2) +
-              16u * static_cast<uint32_t>((lane % 8) ^ (row % 8));
+              16u * static_cast<uint32_t>((lane % 8) ^ ((row >> 1) % 8));
   }
   // Weight piece p = kHugeWLoads * wave + s is bytes 256p .. 256p + 255 of
   // the chunk's 256 rows x 40 bytes; rows past n copy row n - 1 and get zero
@@ -675,7 +678,7 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
       half8 bq[kHugeNSub];
 #pragma unroll
       for (int j = 0; j < kHugeNSub; ++j) bq[j] = dequant8<kHugeLut>(cw[j][t], sc[j], lutp);
-      const int slot = (2 * grp + t) ^ (r % 8);
+      const int slot = (2 * grp + t) ^ ((r >> 1) % 8);
 #pragma unroll
       for (int i = 0; i < kHugeMSub; ++i) {
         const half8 aq = *reinterpret_cast<const half8 *>(
