@@ -120,7 +120,23 @@ def dense_leg(torch, np, ops, I, wl, steps, warmup, copies, dev, sb):
     ms_kernel = ms_step if wl.m <= 16 else time_loop(torch, kernel, steps, warmup)
     packed_bytes = packed.numel()
     flops = 2.0 * wl.m * wl.n * wl.k
-    return dict(ms_step=ms_step, ms_kernel=ms_kernel, packed_bytes=packed_bytes, flops=flops)
+    r = dict(ms_step=ms_step, ms_kernel=ms_kernel, packed_bytes=packed_bytes, flops=flops)
+    if wl.m <= 16:
+        # read ceiling: one plain streaming-read launch over the same packed
+        # bytes, rotating over the same copies
+        sink = torch.zeros(256, dtype=torch.float32, device=dev)
+        r["ms_read"] = time_loop(torch, lambda i: ops.read_probe(stack[i % copies], sink),
+                                 steps, warmup)
+    else:
+        # context: the vendor BLAS (torch.matmul -> hipBLASLt) on a dense fp16
+        # GEMM of the same shape, fp16 out, weights already dense fp16
+        a16 = xt.view(torch.float16)
+        b16 = torch.randn((wl.n, wl.k), device=dev).to(torch.float16)
+        c16 = torch.empty((wl.m, wl.n), dtype=torch.float16, device=dev)
+        r["ms_dense_fp16_blas"] = time_loop(
+            torch, lambda i: torch.matmul(a16, b16.t(), out=c16), steps, warmup)
+        del b16, c16
+    return r
 
 
 def moe_setup(torch, np, ops, I, dev, sb, n1=1856, k=2688, n_exp=128):
@@ -246,13 +262,19 @@ def main() -> int:
     r = dense_leg(torch, np, ops, I, wl, args.steps, args.warmup, args.copies, dev, sb)
     gbs = r["packed_bytes"] / (r["ms_step"] * 1e-3) / 1e9
     k_gbs = r["packed_bytes"] / (r["ms_kernel"] * 1e-3) / 1e9
+    read_gbs = r["packed_bytes"] / (r["ms_read"] * 1e-3) / 1e9
     log(f"dense_m16: step {r['ms_step'] * 1e3:.2f} us ({gbs:.0f} GB/s), "
-        f"dequant-GEMM kernel {r['ms_kernel'] * 1e3:.2f} us ({k_gbs:.0f} GB/s)")
+        f"dequant-GEMM kernel {r['ms_kernel'] * 1e3:.2f} us ({k_gbs:.0f} GB/s), "
+        f"plain read of the same bytes {r['ms_read'] * 1e3:.2f} us ({read_gbs:.0f} GB/s)")
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                 "traffic": load_traffic("dense_m16"),
                 "kernel": "skinny_dma_kernel (the whole tq4_linear call), algorithmic bytes per "
-                          f"launch = packed weights {r['packed_bytes']}"}
+                          f"launch = packed weights {r['packed_bytes']}",
+                "measured_ceiling": {"what": "one streaming-read launch (tq4_read_probe) over "
+                                             "the same packed bytes and copies",
+                                     "GB/s": round(read_gbs, 1),
+                                     "frac_of_ceiling": round(k_gbs / read_gbs, 4)}}
 
     legs = {}
     names = ([] if args.legs == "none" else
@@ -267,11 +289,17 @@ def main() -> int:
             q = dense_leg(torch, np, ops, I, wl2, s2, max(2, args.warmup // 10), 2, dev, sb)
             tf = q["flops"] / (q["ms_step"] * 1e-3) / 1e12
             ktf = q["flops"] / (q["ms_kernel"] * 1e-3) / 1e12
+            btf = q["flops"] / (q["ms_dense_fp16_blas"] * 1e-3) / 1e12
             legs[name] = {"ms_per_step": round(q["ms_step"], 4), "TFLOP/s": round(tf, 1),
                           "kernel_ms": round(q["ms_kernel"], 4),
                           "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
                                        "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": round(ktf / MFMA_F16_PEAK_TFLOPS, 4)}}
+                                       "frac": round(ktf / MFMA_F16_PEAK_TFLOPS, 4)},
+                          "context_dense_fp16_blas": {
+                              "what": "torch.matmul (hipBLASLt) fp16 x fp16 -> fp16 on the same "
+                                      "shape, weights dense",
+                              "TFLOP/s": round(btf, 1),
+                              "ours_over_blas": round(ktf / btf, 4)}}
         else:
             if experts is None:
                 log("moe: generating and packing 128 experts")

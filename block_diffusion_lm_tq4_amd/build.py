@@ -31,6 +31,7 @@ SOURCES = {
     "gemm.hip": [],
     "skinny.hip": [],
     "moe.hip": [],
+    "probe.hip": [],
 }
 
 ARCH = "gfx950"

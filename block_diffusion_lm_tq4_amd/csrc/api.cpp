@@ -248,4 +248,12 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t 
   return device_status(e);
 }
 
+int tq4_read_probe(const void *src, int64_t bytes, float *sink, void *stream) {
+  if (bytes < 0 || bytes % 16 != 0) return TQ4_E_SHAPE;
+  if (bytes == 0) return TQ4_OK;
+  if (src == nullptr || sink == nullptr) return TQ4_E_NULL;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return TQ4_E_ALIGN;
+  return device_status(tq4::launch_read_probe(src, bytes, sink, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -73,6 +73,9 @@ hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_
                            int64_t n, const MoETile *tiles, const int32_t *n_tiles,
                            float *out, hipStream_t s);
 
+// Streaming read of `bytes` (a multiple of 16) from a 16-byte aligned buffer.
+hipError_t launch_read_probe(const void *src, int64_t bytes, float *sink, hipStream_t s);
+
 hipError_t launch_combine(const float *o, const int32_t *inv, const float *topk_w,
                           int64_t t, int32_t topk, int64_t k, float *out, hipStream_t s);
 

@@ -184,3 +184,13 @@ def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
         w1_packed.data_ptr(), n1, w2_packed.data_ptr(), sign_bits & 0xFFFFFFFF,
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x.device)))
     return out
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """One streaming read of a whole device buffer (tq4_read_probe), for timing."""
+    _require(buf.is_cuda and buf.is_contiguous(), "buf must be a contiguous device tensor")
+    _cuda_contig(sink, "sink", torch.float32)
+    _require(sink.numel() >= 256, "sink must hold 256 floats")
+    nbytes = buf.numel() * buf.element_size()
+    check("tq4_read_probe", lib().tq4_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                                 _stream(buf.device)))

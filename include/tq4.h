@@ -170,6 +170,16 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k,
                     const uint8_t *w2_packed, uint32_t sign_bits, float *out,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Measurement aid, not a step of the method: reads `bytes` bytes of device
+ * memory at `src` once (16 bytes per thread, one launch) and discards them.
+ * Timing one call over the footprint of a packed matrix gives the read
+ * ceiling that a single kernel streaming those bytes can reach.
+ *   src  : device, 16-byte aligned; bytes a non-negative multiple of 16
+ *   sink : device fp32[256]; never written for data the library produces
+ * Errors: TQ4_E_NULL, TQ4_E_SHAPE (bytes < 0 or not a multiple of 16),
+ * TQ4_E_ALIGN, TQ4_E_DEVICE.  bytes == 0 is a no-op. */
+int tq4_read_probe(const void *src, int64_t bytes, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -140,6 +140,15 @@ def test_route_argument_errors(L):
     assert L.tq4_moe_route(FAKE, 4, 2, 8, FAKE, FAKE + 1, FAKE, FAKE, None) == E_ALIGN
 
 
+def test_read_probe_argument_errors(L):
+    assert L.tq4_read_probe(FAKE, 40, FAKE, None) == E_SHAPE
+    assert L.tq4_read_probe(FAKE, -16, FAKE, None) == E_SHAPE
+    assert L.tq4_read_probe(FAKE, 0, None, None) == OK      # empty: nothing to check
+    assert L.tq4_read_probe(None, 64, FAKE, None) == E_NULL
+    assert L.tq4_read_probe(FAKE, 64, None, None) == E_NULL
+    assert L.tq4_read_probe(FAKE + 8, 64, FAKE, None) == E_ALIGN
+
+
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(_lib, "_lib", None)

@@ -243,6 +243,16 @@ def test_linear_k0_writes_zeros(dev):
     assert not y.any()
 
 
+def test_read_probe_reads_and_keeps_nothing(dev):
+    # the streaming-read reference used by the bench: runs over a buffer with
+    # a ragged last workgroup and leaves its sink untouched
+    buf = torch.randint(0, 255, (16 * 1000 + 16 * 37,), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    _ops().read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert not sink.any()
+
+
 # ---------------------------------------------------------------------------- MoE
 
 @pytest.fixture(scope="module")
