@@ -49,7 +49,7 @@ int check_workspace(const void *ws, size_t bytes, size_t need) {
 
 // ---- tq4_moe_grouped workspace ------------------------------------------
 struct MoELayout {
-  size_t counts, offsets, perm, inv, tiles, meta, xt, h, ht, o, total;
+  size_t counts, offsets, perm, inv, tiles, meta, xt, ht, o, total;
 };
 
 MoELayout moe_layout(int64_t t, int32_t topk, int32_t e, int64_t n1, int64_t k,
@@ -64,7 +64,6 @@ MoELayout moe_layout(int64_t t, int32_t topk, int32_t e, int64_t n1, int64_t k,
   l.tiles = off;   off += align_up(sizeof(MoETile) * p.max_tiles);
   l.meta = off;    off += kAlign;  // [0] tile count, [1] bad-id count
   l.xt = off;      off += align_up(static_cast<size_t>(t) * k * 2);
-  l.h = off;       off += align_up(pairs * n1 * 4);
   l.ht = off;      off += align_up(pairs * n1 * 2);
   l.o = off;       off += align_up(pairs * k * 4);
   l.total = off;
@@ -230,7 +229,6 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t 
   MoETile *tiles = reinterpret_cast<MoETile *>(ws + l.tiles);
   int32_t *meta = reinterpret_cast<int32_t *>(ws + l.meta);
   uint16_t *xt = reinterpret_cast<uint16_t *>(ws + l.xt);
-  float *h = reinterpret_cast<float *>(ws + l.h);
   uint16_t *ht = reinterpret_cast<uint16_t *>(ws + l.ht);
   float *o = reinterpret_cast<float *>(ws + l.o);
   const int64_t pairs = t * topk;
@@ -240,10 +238,11 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t 
                                    tiles, meta, p.tile_rows, nullptr, s);
   if (e == hipSuccess) e = tq4::launch_act_rht_bf16(x_bf16, t, k, sign_bits, xt, s);
   if (e == hipSuccess)
-    e = tq4::launch_moe_gemm(p, 0, xt, k, perm, topk, w1_packed, n1, tiles, meta, h, s);
-  if (e == hipSuccess) e = tq4::launch_act_rht_f32(h, pairs, n1, sign_bits, ht, s);
+    e = tq4::launch_moe_gemm(p, 0, xt, k, perm, topk, w1_packed, n1, tiles, meta, nullptr, ht,
+                             sign_bits, s);
   if (e == hipSuccess)
-    e = tq4::launch_moe_gemm(p, 1, ht, n1, perm, topk, w2_packed, k, tiles, meta, o, s);
+    e = tq4::launch_moe_gemm(p, 1, ht, n1, perm, topk, w2_packed, k, tiles, meta, o, nullptr,
+                             sign_bits, s);
   if (e == hipSuccess) e = tq4::launch_combine(o, inv, topk_w, t, topk, k, out, s);
   return device_status(e);
 }

@@ -30,7 +30,8 @@
 //
 // MoE.  The same core runs over a device-built list of (expert, first row,
 // rows) tiles.  Mode up gathers activation rows through the bucket
-// permutation and stores relu(acc)^2; mode down reads the bucketed hidden
+// permutation and stores relu(acc)^2 already rotated for the down
+// projection (fp16, one 32-block per wave); mode down reads the bucketed hidden
 // rows and stores acc.  Tiles past the device-side count exit at once, so the
 // grid is sized on the host from t*topk without a sync.
 #include "tq4_internal.h"
@@ -50,6 +51,7 @@ struct GemmArgs {
   const uint16_t *a;         // rotated activations (fp16 bits), row stride k
   const uint8_t *w;          // packed weights [n][k/32][20] (per expert for MoE)
   float *out;                // output rows, stride n
+  uint16_t *out16;           // MoE up: rotated hidden rows (fp16 bits), stride n
   float *partial;            // [ksplit][m][n] (dense split-K)
   const int32_t *perm;       // MoE: bucket position -> pair
   const MoETile *tiles;      // MoE tile list
@@ -60,6 +62,7 @@ struct GemmArgs {
   int32_t ksplit;
   int32_t chunks;            // ceil(k / 128)
   int32_t tiles_m, tiles_n;  // dense: workgroup tiles along m and n
+  uint32_t sign_bits;        // MoE up: rotation signs of the hidden rows
   Codebook cb;
 };
 
@@ -286,6 +289,89 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
           if (m < g.m && n < g.n) dst[m * g.n + n] = acc[i][j][v];
         }
       }
+  } else if constexpr (MODE == kMoEUp) {
+    // h = relu(u)^2, then its rotation ht = H32 diag(s) h / sqrt(32), stored
+    // as fp16: a wave's 32 output columns are one 32-block of h (NSUB == 2).
+    // The wave parks its rows of h in LDS (rows 0-7 of every 16-row tile in
+    // abuf0, rows 8-15 in abuf1; 8 * MSUB staged rows x 32 per wave and
+    // buffer, 16-byte column groups XOR-swizzled by (row / 2) % 8); then two
+    // lanes per staged row rotate it in registers: lane parity p holds
+    // elements 16p .. 16p + 15, rotated in-lane over bits 0-3 of the element
+    // index, and bit 4 pairs the two lanes (a quad-permute exchange).  Each
+    // lane writes 32 contiguous bytes.
+    static_assert(NSUB == 2, "one 32-block of hidden units per wave");
+    static_assert(kWaves * 8 * MSUB * 32 * 4 <= TM * kChunkBytes, "staging fits");
+    __syncthreads();  // every wave is done with the activation stages
+    float *const hs0 = reinterpret_cast<float *>(abuf0) + wave * (8 * MSUB * 32);
+    float *const hs1 = reinterpret_cast<float *>(abuf1) + wave * (8 * MSUB * 32);
+    {
+      float *const hw = (grp >> 1) ? hs1 : hs0;
+#pragma unroll
+      for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float u = acc[i][j][v];
+            const int srow = 8 * i + 4 * (grp & 1) + v;
+            hw[srow * 32 + ((16 * j + r) ^ (4 * ((srow >> 1) & 7)))] = u > 0.f ? u * u : 0.f;
+          }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own writes are visible
+    const int64_t col0 = n_base + wave * 32;
+    const float rs32 = 0x1.6a09e6p-3f;
+    const int p = lane & 1;
+    const int srow = (lane >> 1) < 8 * MSUB ? (lane >> 1) : 0;
+    const int key = 4 * ((srow >> 1) & 7);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const float *hs = half ? hs1 : hs0;
+      const int64_t local = 16 * (srow / 8) + 8 * half + srow % 8;
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f =
+            *reinterpret_cast<const float4 *>(hs + srow * 32 + ((16 * p + 4 * q) ^ key));
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((g.sign_bits >> (16 * p + e)) & 1u) v[e] = -v[e];
+#pragma unroll
+      for (int hstep = 1; hstep < 16; hstep <<= 1)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if ((e & hstep) == 0) {
+            const float a = v[e], b = v[e + hstep];
+            v[e] = a + b;
+            v[e + hstep] = a - b;
+          }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float o = __builtin_bit_cast(
+            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[e]), 0xB1, 0xF, 0xF, false));
+        v[e] = p ? o - v[e] : v[e] + o;
+      }
+      if ((lane >> 1) < 8 * MSUB && local < rows_valid && col0 < g.n) {
+        uint4 *dst = reinterpret_cast<uint4 *>(g.out16 + (m_base + local) * g.n + col0 + 16 * p);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint32_t w[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t lo =
+                __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[8 * q + 2 * t] * rs32));
+            const uint32_t hi =
+                __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[8 * q + 2 * t + 1] * rs32));
+            w[t] = lo | (hi << 16);
+          }
+          dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
@@ -295,13 +381,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int64_t local = 16 * i + 4 * grp + v;
-          if (local < rows_valid && n < g.n) {
-            float val = acc[i][j][v];
-            if constexpr (MODE == kMoEUp) {
-              val = val > 0.f ? val * val : 0.f;
-            }
-            g.out[(m_base + local) * g.n + n] = val;
-          }
+          if (local < rows_valid && n < g.n) g.out[(m_base + local) * g.n + n] = acc[i][j][v];
         }
       }
   }
@@ -849,11 +929,14 @@ MoEPlan plan_moe(int64_t pairs, int32_t n_experts) {
 hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_t k,
                            const int32_t *perm, int32_t topk, const uint8_t *w_packed, int64_t n,
                            const MoETile *tiles, const int32_t *n_tiles, float *out,
-                           hipStream_t s) {
+                           uint16_t *out16, uint32_t sign_bits, hipStream_t s) {
+  if (mode == 0 && n % 32 != 0) return hipErrorInvalidValue;
   GemmArgs g{};
   g.a = a;
   g.w = w_packed;
   g.out = out;
+  g.out16 = out16;
+  g.sign_bits = sign_bits;
   g.perm = perm;
   g.tiles = tiles;
   g.n_tiles = n_tiles;

@@ -29,19 +29,6 @@ __device__ inline void load_block<uint16_t>(const uint16_t *p, float (&v)[32]) {
   }
 }
 
-template <>
-__device__ inline void load_block<float>(const float *p, float (&v)[32]) {
-  const float4 *q = reinterpret_cast<const float4 *>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 d = q[i];
-    v[4 * i] = d.x;
-    v[4 * i + 1] = d.y;
-    v[4 * i + 2] = d.z;
-    v[4 * i + 3] = d.w;
-  }
-}
-
 template <typename In>
 __global__ __launch_bounds__(256) void act_rht_kernel(const In *__restrict__ x, int64_t n_blocks,
                                                       uint32_t sign_bits,
@@ -109,11 +96,6 @@ hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s) {
 hipError_t launch_act_rht_bf16(const uint16_t *x, int64_t m, int64_t k, uint32_t sign_bits,
                                uint16_t *xt, hipStream_t s) {
   return launch<uint16_t>(x, m, k, sign_bits, xt, s);
-}
-
-hipError_t launch_act_rht_f32(const float *x, int64_t m, int64_t k, uint32_t sign_bits,
-                              uint16_t *xt, hipStream_t s) {
-  return launch<float>(x, m, k, sign_bits, xt, s);
 }
 
 }  // namespace tq4

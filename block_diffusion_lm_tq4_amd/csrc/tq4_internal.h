@@ -18,11 +18,9 @@ const Codebook &codebook();
 hipError_t launch_pack(const float *w, int64_t n_blocks, uint32_t sign_bits,
                        uint8_t *packed, int32_t *nonfinite, hipStream_t s);
 
-// Rotate [m, k] rows (bf16 or fp32) to fp16.
+// Rotate [m, k] bf16 rows to fp16.
 hipError_t launch_act_rht_bf16(const uint16_t *x, int64_t m, int64_t k, uint32_t sign_bits,
                                uint16_t *xt, hipStream_t s);
-hipError_t launch_act_rht_f32(const float *x, int64_t m, int64_t k, uint32_t sign_bits,
-                              uint16_t *xt, hipStream_t s);
 
 hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s);
 
@@ -66,12 +64,13 @@ struct MoEPlan {
 MoEPlan plan_moe(int64_t pairs, int32_t n_experts);
 
 // Grouped product over MoE tiles.  mode 0 (up): A rows gathered through
-// perm[]/topk from xt [t, k]; output h[row, n] = relu(acc)^2 (fp32).
-// mode 1 (down): A rows are the bucket rows of ht [pairs, k]; output o[row, n].
+// perm[]/topk from xt [t, k]; output out16[row, n] = the rotation (sign_bits,
+// per 32-block, fp16) of relu(acc)^2, n % 32 == 0.  mode 1 (down): A rows are
+// the bucket rows of ht [pairs, k]; output out[row, n] = acc (fp32).
 hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_t k,
                            const int32_t *perm, int32_t topk, const uint8_t *w_packed,
                            int64_t n, const MoETile *tiles, const int32_t *n_tiles,
-                           float *out, hipStream_t s);
+                           float *out, uint16_t *out16, uint32_t sign_bits, hipStream_t s);
 
 // Streaming read of `bytes` (a multiple of 16) from a 16-byte aligned buffer.
 hipError_t launch_read_probe(const void *src, int64_t bytes, float *sink, hipStream_t s);
