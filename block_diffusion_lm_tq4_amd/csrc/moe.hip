@@ -77,20 +77,49 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     tile_base[e] = tile_rows > 0 ? (run + tile_rows - 1) / tile_rows : 0;
   }
   __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0, trun = 0;
-    for (int e = 0; e < n_experts; ++e) {
-      const int32_t c = base[e], tc = tile_base[e];
-      base[e] = run;
-      tile_base[e] = trun;
-      offsets[e] = run;
-      run += c;
-      trun += tc;
+  // exclusive scans of the counts and tile counts over the experts, by wave
+  // 0: lane l sums experts 8l .. 8l + 7, then the lanes' totals are scanned
+  if (wave == 0) {
+    constexpr int kPer = kMaxExperts / 64;
+    int32_t c[kPer], tc[kPer];
+    int32_t sum = 0, tsum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = kPer * lane + i;
+      c[i] = e < n_experts ? base[e] : 0;
+      tc[i] = e < n_experts ? tile_base[e] : 0;
+      sum += c[i];
+      tsum += tc[i];
     }
-    base[n_experts] = run;
-    offsets[n_experts] = run;
-    tile_base[n_experts] = trun;
-    if (n_tiles != nullptr) *n_tiles = trun;
+    int32_t run = sum, trun = tsum;  // inclusive scan over lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t a = __shfl_up(run, d);
+      const int32_t b = __shfl_up(trun, d);
+      if (lane >= d) {
+        run += a;
+        trun += b;
+      }
+    }
+    run -= sum;
+    trun -= tsum;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = kPer * lane + i;
+      if (e < n_experts) {
+        base[e] = run;
+        tile_base[e] = trun;
+        offsets[e] = run;
+      }
+      run += c[i];
+      trun += tc[i];
+    }
+    if (lane == 63) {
+      base[n_experts] = run;
+      offsets[n_experts] = run;
+      tile_base[n_experts] = trun;
+      if (n_tiles != nullptr) *n_tiles = trun;
+    }
   }
   __syncthreads();
 
@@ -130,29 +159,30 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 }
 
 // out[t, :] = sum_j w[t, j] * o[inv[t*topk + j], :] in slot order; each thread
-// owns four consecutive features of one token.
+// owns four consecutive features of a token (grid: feature groups x tokens,
+// tokens strided by the grid height).
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o,
                                                       const int32_t *__restrict__ inv,
                                                       const float *__restrict__ topk_w,
                                                       int64_t t, int32_t topk, int64_t k,
                                                       float *__restrict__ out) {
   const int64_t q = k / 4;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= t * q) return;
-  const int64_t tok = idx / q;
-  const int64_t c = idx % q;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < topk; ++j) {
-    const int32_t row = inv[tok * topk + j];
-    if (row < 0) continue;
-    const float gw = topk_w[tok * topk + j];
-    const float4 v = reinterpret_cast<const float4 *>(o + static_cast<int64_t>(row) * k)[c];
-    s.x += gw * v.x;
-    s.y += gw * v.y;
-    s.z += gw * v.z;
-    s.w += gw * v.w;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= q) return;
+  for (int64_t tok = blockIdx.y; tok < t; tok += gridDim.y) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < topk; ++j) {
+      const int32_t row = inv[tok * topk + j];
+      if (row < 0) continue;
+      const float gw = topk_w[tok * topk + j];
+      const float4 v = reinterpret_cast<const float4 *>(o + static_cast<int64_t>(row) * k)[c];
+      acc.x += gw * v.x;
+      acc.y += gw * v.y;
+      acc.z += gw * v.z;
+      acc.w += gw * v.w;
+    }
+    reinterpret_cast<float4 *>(out + tok * k)[c] = acc;
   }
-  reinterpret_cast<float4 *>(out + tok * k)[c] = s;
 }
 
 }  // namespace
@@ -170,10 +200,11 @@ hipError_t launch_route(const int32_t *ids, int64_t pairs, int32_t topk, int32_t
 
 hipError_t launch_combine(const float *o, const int32_t *inv, const float *topk_w, int64_t t,
                           int32_t topk, int64_t k, float *out, hipStream_t s) {
-  const int64_t work = t * (k / 4);
-  if (work == 0) return hipSuccess;
+  const int64_t q = k / 4;
+  if (t == 0 || q == 0) return hipSuccess;
   const int threads = 256;
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((work + threads - 1) / threads)),
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((q + threads - 1) / threads),
+                                          static_cast<unsigned>(t < 65535 ? t : 65535)),
                      dim3(threads), 0, s, o, inv, topk_w, t, topk, k, out);
   return hipGetLastError();
 }
