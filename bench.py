@@ -35,30 +35,30 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
-KERNEL_SOURCES = ("skinny.hip",)  # the M<=16 kernel the traffic record describes
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "block_diffusion_lm_tq4_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def load_traffic(key: str):
-    """HBM bytes per launch from committed PMC counters, if they match the source."""
+    """HBM bytes per launch from committed PMC counters, if they match the
+    current source of the kernel they were taken on (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:
             rec = json.load(fh).get(key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != kernel_source_sha():
+    if not rec or rec.get("source_sha") != kernel_source_sha(rec.get("sources", ())):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -294,7 +294,10 @@ def main() -> int:
                           "kernel_ms": round(q["ms_kernel"], 4),
                           "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
                                        "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": round(ktf / MFMA_F16_PEAK_TFLOPS, 4)},
+                                       "frac": round(ktf / MFMA_F16_PEAK_TFLOPS, 4),
+                                       "traffic": load_traffic(name),
+                                       "kernel": "gemm_huge_kernel (tq4_linear_rotated), "
+                                                 "2*M*N*K flops per launch"},
                           "context_dense_fp16_blas": {
                               "what": "torch.matmul (hipBLASLt) fp16 x fp16 -> fp16 on the same "
                                       "shape, weights dense",
