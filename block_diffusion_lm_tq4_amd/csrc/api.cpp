@@ -235,8 +235,8 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t 
   hipStream_t s = as_stream(stream);
 
   hipError_t e = tq4::launch_route(topk_ids, pairs, topk, n_experts, counts, offsets, perm, inv,
-                                   tiles, meta, p.tile_rows, nullptr, s);
-  if (e == hipSuccess) e = tq4::launch_act_rht_bf16(x_bf16, t, k, sign_bits, xt, s);
+                                   tiles, meta, p.tile_rows, nullptr, s, x_bf16, t * (k / 32),
+                                   sign_bits, xt);
   if (e == hipSuccess)
     e = tq4::launch_moe_gemm(p, 0, xt, k, perm, topk, w1_packed, n1, tiles, meta, nullptr, ht,
                              sign_bits, s);

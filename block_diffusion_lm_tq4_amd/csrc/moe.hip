@@ -35,12 +35,19 @@ __device__ inline uint64_t same_key_lanes(int key, uint64_t active, int key_bits
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int32_t *__restrict__ ids, int64_t pairs, int32_t n_experts, int32_t *counts,
     int32_t *offsets, int32_t *perm, int32_t *inv, MoETile *tiles, int32_t *n_tiles,
-    int32_t tile_rows, int32_t *status) {
+    int32_t tile_rows, int32_t *status, const uint16_t *__restrict__ x, int64_t x_blocks,
+    uint32_t sign_bits, uint16_t *__restrict__ xt) {
   __shared__ int32_t hist[kRouteWaves][kMaxExperts];
   __shared__ int32_t base[kMaxExperts + 1];
   __shared__ int32_t tile_base[kMaxExperts + 1];
 
   const int tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    // the activation rotation of the same layer rides along in this launch
+    const int64_t blk = static_cast<int64_t>(blockIdx.x - 1) * kRouteThreads + tid;
+    if (blk < x_blocks) rotate_block_bf16(x + blk * 32, sign_bits, xt + blk * 32);
+    return;
+  }
   const int wave = tid / 64;
   const int lane = tid % 64;
   int key_bits = 0;
@@ -190,11 +197,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 hipError_t launch_route(const int32_t *ids, int64_t pairs, int32_t topk, int32_t n_experts,
                         int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                         MoETile *tiles, int32_t *n_tiles, int32_t tile_rows, int32_t *status,
-                        hipStream_t s) {
+                        hipStream_t s, const uint16_t *x, int64_t x_blocks, uint32_t sign_bits,
+                        uint16_t *xt) {
   (void)topk;
   if (n_experts > kMaxExperts) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, pairs, n_experts,
-                     counts, offsets, perm, inv, tiles, n_tiles, tile_rows, status);
+  const int64_t rot_wgs = x != nullptr ? (x_blocks + kRouteThreads - 1) / kRouteThreads : 0;
+  hipLaunchKernelGGL(route_kernel, dim3(static_cast<unsigned>(1 + rot_wgs)), dim3(kRouteThreads),
+                     0, s, ids, pairs, n_experts, counts, offsets, perm, inv, tiles, n_tiles,
+                     tile_rows, status, x, x_blocks, sign_bits, xt);
   return hipGetLastError();
 }
 

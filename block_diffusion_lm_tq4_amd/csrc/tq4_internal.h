@@ -14,6 +14,54 @@ struct Codebook {
 // Lloyd-Max levels of N(0,1) rounded to fp32, computed once on the host.
 const Codebook &codebook();
 
+// xt = H32 diag(s) x / sqrt(32) of one 32-element block: bf16 in (16-byte
+// aligned), fp32 butterfly in natural (Sylvester) order, fp16 out.  The format
+// rotates every weight block by this orthogonal matrix (Nemotron-TheHobbit-
+// 30B-A3B model card, What "Config-I" means), so rotating the activations
+// instead leaves the weight side of a product as lookups times scales.
+__device__ inline void rotate_block_bf16(const uint16_t *x, uint32_t sign_bits, uint16_t *xt) {
+  float v[32];
+  const uint4 *q = reinterpret_cast<const uint4 *>(x);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 d = q[i];
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if ((sign_bits >> i) & 1u) v[i] = -v[i];
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+  const float rs32 = 0x1.6a09e6p-3f;  // 1/sqrt(32) rounded to fp32
+  uint4 *dst = reinterpret_cast<uint4 *>(xt);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 lo = static_cast<_Float16>(v[8 * i + 2 * j] * rs32);
+      const _Float16 hi = static_cast<_Float16>(v[8 * i + 2 * j + 1] * rs32);
+      w[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
+    dst[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // ---- launchers (return hipSuccess or the launch error) --------------------
 hipError_t launch_pack(const float *w, int64_t n_blocks, uint32_t sign_bits,
                        uint8_t *packed, int32_t *nonfinite, hipStream_t s);
@@ -51,10 +99,14 @@ struct MoETile {  // one m-tile of one expert's segment in bucket order
   int32_t rows;   // rows in this tile (<= tile height)
   int32_t pad;
 };
+// Bucketing (one workgroup).  With x != nullptr the same launch also rotates
+// the [t, k] bf16 activation rows into xt (extra workgroups, one thread per
+// 32-block).
 hipError_t launch_route(const int32_t *ids, int64_t pairs, int32_t topk, int32_t n_experts,
                         int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                         MoETile *tiles, int32_t *n_tiles, int32_t tile_rows,
-                        int32_t *status, hipStream_t s);
+                        int32_t *status, hipStream_t s, const uint16_t *x = nullptr,
+                        int64_t x_blocks = 0, uint32_t sign_bits = 0, uint16_t *xt = nullptr);
 
 struct MoEPlan {
   int msub, nsub, waves_m, waves_n;
