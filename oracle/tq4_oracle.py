@@ -66,6 +66,7 @@ __all__ = [
     "linear",
     "moe",
     "bucket_pairs",
+    "router",
     "packed_size",
 ]
 
@@ -346,3 +347,37 @@ def bucket_pairs(topk_ids: np.ndarray, n_experts: int):
     inv = np.full(ids.shape[0], -1, dtype=np.int32)
     inv[perm] = np.arange(perm.shape[0], dtype=np.int32)
     return counts, offsets, perm, inv
+
+
+def router(logits: np.ndarray, topk: int):
+    """The MoE router before the layer (model card, The model underneath:
+    128 experts, top-6): softmax over all expert logits of a token, then the
+    topk experts with the largest logits, ties to the lower expert id; each
+    gate is that expert's softmax probability, not renormalized over the k.
+
+    logits [T, E] (any float dtype, read exactly); returns (ids int32 [T, k],
+    gates fp64 [T, k]) with ids in decreasing logit order.  Plain per-token
+    loops, fp64 arithmetic.
+    """
+    lg = np.asarray(logits, dtype=np.float64)
+    t, e = lg.shape
+    ids = np.zeros((t, topk), dtype=np.int32)
+    gates = np.zeros((t, topk), dtype=np.float64)
+    for i in range(t):
+        row = lg[i]
+        mx = max(row)
+        ex = [np.exp(v - mx) for v in row]
+        total = sum(ex)
+        taken = set()
+        for j in range(topk):
+            best = -1
+            for c in range(e):
+                if c in taken:
+                    continue
+                if best < 0 or row[c] > row[best]:
+                    best = c
+            taken.add(best)
+            ids[i, j] = best
+            gates[i, j] = ex[best] / total
+    return ids, gates
+

@@ -150,3 +150,38 @@ def test_router_top6_is_softmax_of_largest():
     pz = np.arange(1, 129, dtype=np.float64) ** -1.1
     pz /= pz.sum()
     assert abs(freq[0] - pz[0]) < 0.01 and abs(freq[1] - pz[1]) < 0.01
+
+
+def test_oracle_router_closed_form_and_ties():
+    # logits ln(1..8): softmax probabilities are exactly (1..8)/36
+    lg = np.log(np.arange(1, 9, dtype=np.float64))[None, :]
+    ids, g = O.router(lg, 3)
+    assert ids.tolist() == [[7, 6, 5]]
+    assert np.allclose(g, [[8 / 36, 7 / 36, 6 / 36]], rtol=1e-14)
+    # all logits equal: the lowest ids win, every gate is 1/E
+    ids, g = O.router(np.full((2, 16), 0.25), 4)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 2
+    assert np.allclose(g, 1 / 16, rtol=1e-14)
+    # partial ties: among equal logits the lower id comes first
+    lt = np.array([[1.0, 3.0, 2.0, 3.0, 2.0, -1.0]])
+    ids, _ = O.router(lt, 5)
+    assert ids.tolist() == [[1, 3, 2, 4, 0]]
+    # a constant shift of the logits changes nothing
+    r = np.random.default_rng(7).standard_normal((5, 32))
+    a = O.router(r, 6)
+    b = O.router(r + 123.0, 6)
+    assert np.array_equal(a[0], b[0]) and np.allclose(a[1], b[1], rtol=1e-12)
+
+
+def test_oracle_router_brute_force_small():
+    # every permutation of 5 distinct logits: the ids are the argsort, the
+    # gates the softmax of the picked ones
+    import itertools
+    base = np.array([-1.5, -0.25, 0.0, 0.75, 2.0])
+    for perm in itertools.permutations(range(5)):
+        lg = base[list(perm)][None, :]
+        ids, g = O.router(lg, 3)
+        order = sorted(range(5), key=lambda c: (-lg[0, c], c))[:3]
+        assert ids[0].tolist() == order
+        p = np.exp(lg[0]) / np.exp(lg[0]).sum()
+        assert np.allclose(g[0], p[order], rtol=1e-13)
