@@ -168,10 +168,16 @@ def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb):
         ops.moe_grouped(x, idt, gt, experts[0], experts[1], sb, out=out, workspace=ws)
 
     ms = time_loop(torch, step, steps, warmup)
+    # the router in front of the layer (softmax + top-k on the device), on the
+    # logits these ids came from
+    lg = torch.from_numpy(I.router_logits(wl.t, wl.n_experts, wl.routing).astype(np.float32)).to(dev)
+    r_ids = torch.empty_like(idt)
+    r_g = torch.empty_like(gt)
+    ms_router = time_loop(torch, lambda i: ops.moe_router(lg, wl.topk, r_ids, r_g), steps, warmup)
     touched = np.unique(ids).size
     per_expert = (wl.n1 * (wl.k // 32) + wl.k * (wl.n1 // 32)) * 20
     pairs = wl.t * wl.topk
-    return dict(ms_step=ms, packed_bytes=touched * per_expert,
+    return dict(ms_step=ms, ms_router=ms_router, packed_bytes=touched * per_expert,
                 flops=2.0 * pairs * 2 * wl.n1 * wl.k, experts_touched=int(touched))
 
 
@@ -314,6 +320,7 @@ def main() -> int:
             tf = q["flops"] / (q["ms_step"] * 1e-3) / 1e12
             legs[name] = {"ms_per_step": round(q["ms_step"], 4), "GB/s": round(g2, 1),
                           "TFLOP/s": round(tf, 2), "experts_touched": q["experts_touched"],
+                          "router_us": round(q["ms_router"] * 1e3, 2),
                           "roofline": {"bound": "hbm", "achieved": round(g2, 1),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": round(g2 / HBM_PEAK_GBS, 4)}}

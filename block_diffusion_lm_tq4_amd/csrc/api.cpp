@@ -255,4 +255,16 @@ int tq4_read_probe(const void *src, int64_t bytes, float *sink, void *stream) {
   return device_status(tq4::launch_read_probe(src, bytes, sink, as_stream(stream)));
 }
 
+int tq4_moe_router(const float *logits, int64_t t, int32_t n_experts, int32_t topk,
+                   int32_t *topk_ids, float *topk_w, void *stream) {
+  if (t < 0 || n_experts < 1 || n_experts > 512 || topk < 1 || topk > n_experts)
+    return TQ4_E_SHAPE;
+  if (t > (int64_t{1} << 33)) return TQ4_E_SHAPE;  // grid of t / 4 workgroups
+  if (t == 0) return TQ4_OK;
+  if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr) return TQ4_E_NULL;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return TQ4_E_ALIGN;
+  return device_status(
+      tq4::launch_router(logits, t, n_experts, topk, topk_ids, topk_w, as_stream(stream)));
+}
+
 }  // extern "C"

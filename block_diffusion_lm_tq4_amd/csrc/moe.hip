@@ -192,6 +192,67 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   }
 }
 
+// The router in front of the layer (model card, The model underneath: 128
+// experts, top-6), one wave per token: softmax over all expert logits, then
+// the topk largest logits with ties to the lower expert id, each gate the
+// expert's softmax probability (not renormalized).  Lane l holds experts
+// l, l + 64, ...; the max, the sum and every arg-max are xor-butterfly
+// reductions, which leave bit-identical results in all lanes.
+constexpr int kRouterPer = kMaxExperts / 64;
+
+__global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ logits, int64_t t,
+                                                     int32_t n_experts, int32_t topk,
+                                                     int32_t *__restrict__ ids,
+                                                     float *__restrict__ gates) {
+  const int64_t tok = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  if (tok >= t) return;
+  const int lane = threadIdx.x % 64;
+  const float *row = logits + tok * n_experts;
+  float v[kRouterPer];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < kRouterPer; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < n_experts ? row[e] : -__builtin_inff();
+    mx = fmaxf(mx, v[i]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRouterPer; ++i)
+    if (lane + 64 * i < n_experts) sum += expf(v[i] - mx);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+  uint32_t taken = 0;
+  for (int j = 0; j < topk; ++j) {
+    float bv = -__builtin_inff();
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kRouterPer; ++i) {
+      const int e = lane + 64 * i;
+      if (e < n_experts && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const float ov = __shfl_xor(bv, d);
+      const int oi = __shfl_xor(bi, d);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == bi % 64) taken |= 1u << (bi / 64);
+    if (lane == 0) {
+      ids[tok * topk + j] = bi;
+      gates[tok * topk + j] = expf(bv - mx) / sum;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_route(const int32_t *ids, int64_t pairs, int32_t topk, int32_t n_experts,
@@ -216,6 +277,15 @@ hipError_t launch_combine(const float *o, const int32_t *inv, const float *topk_
   hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((q + threads - 1) / threads),
                                           static_cast<unsigned>(t < 65535 ? t : 65535)),
                      dim3(threads), 0, s, o, inv, topk_w, t, topk, k, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const float *logits, int64_t t, int32_t n_experts, int32_t topk,
+                         int32_t *ids, float *gates, hipStream_t s) {
+  if (n_experts > kMaxExperts) return hipErrorInvalidValue;
+  if (t == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_kernel, dim3(static_cast<unsigned>((t + 3) / 4)), dim3(256), 0, s,
+                     logits, t, n_experts, topk, ids, gates);
   return hipGetLastError();
 }
 

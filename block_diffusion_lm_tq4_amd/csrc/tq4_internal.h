@@ -127,6 +127,11 @@ hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_
 // Streaming read of `bytes` (a multiple of 16) from a 16-byte aligned buffer.
 hipError_t launch_read_probe(const void *src, int64_t bytes, float *sink, hipStream_t s);
 
+// Router: per token, softmax over the n_experts logits, ids of the topk
+// largest (ties to the lower id), gates = their probabilities.
+hipError_t launch_router(const float *logits, int64_t t, int32_t n_experts, int32_t topk,
+                         int32_t *ids, float *gates, hipStream_t s);
+
 hipError_t launch_combine(const float *o, const int32_t *inv, const float *topk_w,
                           int64_t t, int32_t topk, int64_t k, float *out, hipStream_t s);
 

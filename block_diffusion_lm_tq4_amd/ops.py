@@ -151,6 +151,25 @@ def moe_route(topk_ids: torch.Tensor, n_experts: int):
     return counts, offsets, perm, inv
 
 
+def moe_router(logits: torch.Tensor, topk: int,
+               ids: torch.Tensor | None = None, gates: torch.Tensor | None = None):
+    """Router of the MoE layer (tq4_moe_router): (ids int32 [t, topk], gates fp32 [t, topk])."""
+    _cuda_contig(logits, "logits", torch.float32)
+    _require(logits.dim() == 2, "logits must be [t, n_experts]")
+    t, e = logits.shape
+    if ids is None:
+        ids = torch.empty((t, topk), dtype=torch.int32, device=logits.device)
+    if gates is None:
+        gates = torch.empty((t, topk), dtype=torch.float32, device=logits.device)
+    _cuda_contig(ids, "ids", torch.int32)
+    _cuda_contig(gates, "gates", torch.float32)
+    _require(tuple(ids.shape) == (t, topk) and tuple(gates.shape) == (t, topk),
+             "ids and gates must be [t, topk]")
+    check("tq4_moe_router", lib().tq4_moe_router(logits.data_ptr(), t, e, topk, ids.data_ptr(),
+                                                 gates.data_ptr(), _stream(logits.device)))
+    return ids, gates
+
+
 def moe_workspace_size(t: int, topk: int, n_experts: int, n1: int, k: int) -> int:
     return int(lib().tq4_moe_workspace_size(t, topk, n_experts, n1, k))
 

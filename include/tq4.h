@@ -170,6 +170,23 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k,
                     const uint8_t *w2_packed, uint32_t sign_bits, float *out,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* The router in front of the MoE layer (model card, The model underneath:
+ * 128 experts, top-6), on the device so that a layer goes from router logits
+ * to its output without the host:
+ *   per token t: p = softmax(logits[t, :]) over all n_experts;
+ *   topk_ids[t, :] = the topk experts with the largest logits, in decreasing
+ *                    order, ties to the lower expert id;
+ *   topk_w[t, j]   = p[topk_ids[t, j]] (not renormalized over the k).
+ *   logits   : [t, n_experts] fp32, device, finite values
+ *   topk_ids : [t, topk] int32, device, overwritten
+ *   topk_w   : [t, topk] fp32, device, overwritten
+ * Ids are decided on the fp32 logits exactly; gates are fp32 (expf).
+ * Errors: TQ4_E_SHAPE (t < 0 or t > 2^33, n_experts outside 1..512, topk
+ * outside 1..n_experts), TQ4_E_NULL, TQ4_E_ALIGN (4-byte), TQ4_E_DEVICE.
+ * t == 0 is a no-op. */
+int tq4_moe_router(const float *logits, int64_t t, int32_t n_experts, int32_t topk,
+                   int32_t *topk_ids, float *topk_w, void *stream);
+
 /* Measurement aid, not a step of the method: reads `bytes` bytes of device
  * memory at `src` once (16 bytes per thread, one launch) and discards them.
  * Timing one call over the footprint of a packed matrix gives the read

@@ -140,6 +140,19 @@ def test_route_argument_errors(L):
     assert L.tq4_moe_route(FAKE, 4, 2, 8, FAKE, FAKE + 1, FAKE, FAKE, None) == E_ALIGN
 
 
+def test_router_argument_errors(L):
+    assert L.tq4_moe_router(FAKE, -1, 128, 6, FAKE, FAKE, None) == E_SHAPE
+    assert L.tq4_moe_router(FAKE, 4, 0, 1, FAKE, FAKE, None) == E_SHAPE
+    assert L.tq4_moe_router(FAKE, 4, 513, 6, FAKE, FAKE, None) == E_SHAPE
+    assert L.tq4_moe_router(FAKE, 4, 128, 0, FAKE, FAKE, None) == E_SHAPE
+    assert L.tq4_moe_router(FAKE, 4, 8, 9, FAKE, FAKE, None) == E_SHAPE
+    assert L.tq4_moe_router(None, 0, 128, 6, None, None, None) == OK
+    assert L.tq4_moe_router(None, 4, 128, 6, FAKE, FAKE, None) == E_NULL
+    assert L.tq4_moe_router(FAKE, 4, 128, 6, None, FAKE, None) == E_NULL
+    assert L.tq4_moe_router(FAKE, 4, 128, 6, FAKE, None, None) == E_NULL
+    assert L.tq4_moe_router(FAKE + 2, 4, 128, 6, FAKE, FAKE, None) == E_ALIGN
+
+
 def test_read_probe_argument_errors(L):
     assert L.tq4_read_probe(FAKE, 40, FAKE, None) == E_SHAPE
     assert L.tq4_read_probe(FAKE, -16, FAKE, None) == E_SHAPE

@@ -338,6 +338,48 @@ def test_moe_t1024_sampled_tokens(dev, experts, name):
     _check_close(out[tok], ref, name + " (sampled tokens)")
 
 
+@pytest.mark.parametrize("t,e,k,routing", [
+    (1024, 128, 6, "uniform"),       # batched block diffusion, uniform logits
+    (1024, 128, 6, "zipf"),          # Zipf(1.1) expert popularity
+    (16, 128, 6, "uniform"),         # one 16-token block
+    (37, 100, 8, "uniform"),         # experts not a multiple of 64, ragged tokens
+    (5, 512, 16, "zipf"),            # largest expert count
+    (3, 1, 1, "uniform"),            # single expert
+])
+def test_router_matches_oracle(dev, t, e, k, routing):
+    lg = I.router_logits(t, e, routing, seed=11).astype(np.float32)
+    ids, g = _ops().moe_router(torch.from_numpy(lg).to(dev), k)
+    ref_ids, ref_g = O.router(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.allclose(g.cpu().numpy(), ref_g, rtol=2e-6, atol=0)
+
+
+def test_router_ties_and_empty(dev):
+    lg = np.zeros((4, 128), dtype=np.float32)
+    lg[1, [5, 9, 70, 71]] = 1.0           # ties among the top, across lanes
+    lg[2, ::2] = 0.5                      # half the experts tied
+    lg[3] = np.repeat(np.arange(32, dtype=np.float32), 4)  # ties in groups of 4
+    ids, g = _ops().moe_router(torch.from_numpy(lg).to(dev), 6)
+    ref_ids, ref_g = O.router(lg, 6)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.allclose(g.cpu().numpy(), ref_g, rtol=2e-6, atol=0)
+    e_ids, e_g = _ops().moe_router(torch.empty((0, 128), device=dev), 6)
+    assert e_ids.shape == (0, 6) and e_g.shape == (0, 6)
+
+
+def test_moe_from_logits_matches_oracle(dev, experts):
+    # router on the device feeding the grouped layer, against the oracle's
+    # router feeding the oracle's layer (16 tokens, all outputs)
+    wl = I.WORKLOADS["moe_t16"]
+    lg = I.router_logits(wl.t, wl.n_experts, "uniform", seed=5).astype(np.float32)
+    x_bits = I.activations_bf16(wl.t, wl.k)
+    ids, g = _ops().moe_router(torch.from_numpy(lg).to(dev), wl.topk)
+    out = _ops().moe_grouped(_bf16(x_bits, dev), ids, g, experts[0], experts[1], SB)
+    ref_ids, ref_g = O.router(lg, wl.topk)
+    ref = O.moe(x_bits, ref_ids, ref_g, _oracle_expert(experts, 1), _oracle_expert(experts, 2), SB)
+    _check_close(out.cpu().numpy(), ref, "moe from logits")
+
+
 def test_moe_deterministic(dev, experts):
     wl = I.WORKLOADS["moe_t1024_zipf"]
     ids, g = I.moe_routing(wl)
