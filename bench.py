@@ -181,6 +181,24 @@ def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb):
                 flops=2.0 * pairs * 2 * wl.n1 * wl.k, experts_touched=int(touched))
 
 
+def pack_leg(torch, np, ops, I, steps, warmup, dev, sb, n=8192, k=2688):
+    """Offline quantizer throughput (tq4_pack_bf16 and tq4_pack) on one
+    denoiser-projection-sized matrix, weights resident on the device."""
+    w = I.weights(n, k)
+    w32 = torch.from_numpy(w).to(dev)
+    wbf = w32.to(torch.bfloat16)
+    out = torch.empty((n, k // 32, 20), dtype=torch.uint8, device=dev)
+    ms_bf = time_loop(torch, lambda i: ops.pack(wbf, sb, out=out), steps, warmup)
+    ms_32 = time_loop(torch, lambda i: ops.pack(w32, sb, out=out), steps, warmup)
+    wps = n * k / (ms_bf * 1e-3)
+    return {"matrix": f"{n}x{k}", "bf16_in_us": round(ms_bf * 1e3, 2),
+            "fp32_in_us": round(ms_32 * 1e3, 2),
+            "bf16_in_GB/s": round(n * k * 2 / (ms_bf * 1e-3) / 1e9, 1),
+            "weights_per_s": float(f"{wps:.4g}"),
+            "context": "59e9 weights (both towers) at this rate take "
+                       f"{59e9 / wps:.1f} s of kernel time"}
+
+
 # ----------------------------------------------------------------------- CPU side
 
 def cpu_baseline(np, I, budget_s: float = 12.0):
@@ -219,7 +237,7 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=48)
     ap.add_argument("--legs", default="all",
                     help="all | none | comma list of dense_m4096_t3,moe_t16,"
-                         "moe_t1024_uniform,moe_t1024_zipf")
+                         "moe_t1024_uniform,moe_t1024_zipf,pack")
     ap.add_argument("--only", default=None,
                     help="profile helper: run just this workload (no JSON contract)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -284,10 +302,15 @@ def main() -> int:
 
     legs = {}
     names = ([] if args.legs == "none" else
-             ["dense_m4096_t3", "moe_t16", "moe_t1024_uniform", "moe_t1024_zipf"]
+             ["dense_m4096_t3", "moe_t16", "moe_t1024_uniform", "moe_t1024_zipf", "pack"]
              if args.legs == "all" else args.legs.split(","))
     experts = None
     for name in names:
+        if name == "pack":
+            log("pack: running")
+            legs[name] = pack_leg(torch, np, ops, I, max(5, args.steps // 20), 2, dev, sb)
+            log(name, json.dumps(legs[name]))
+            continue
         wl2 = I.WORKLOADS[name]
         if name.startswith("dense"):
             log(f"{name}: running")

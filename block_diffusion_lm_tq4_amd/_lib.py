@@ -34,6 +34,7 @@ SIGNATURES = {
     "tq4_codebook": (ctypes.c_int, [_P]),
     "tq4_packed_size": (_SZ, [_I64, _I64]),
     "tq4_pack": (ctypes.c_int, [_P, _I64, _I64, _U32, _P, _P, _P]),
+    "tq4_pack_bf16": (ctypes.c_int, [_P, _I64, _I64, _U32, _P, _P, _P]),
     "tq4_act_rht": (ctypes.c_int, [_P, _I64, _I64, _U32, _P, _P]),
     "tq4_linear_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "tq4_linear": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _U32, _P, _P, _SZ, _P]),

@@ -120,6 +120,18 @@ int tq4_pack(const float *w, int64_t n, int64_t k, uint32_t sign_bits, uint8_t *
       tq4::launch_pack(w, n * (k / 32), sign_bits, packed, nonfinite_count, as_stream(stream)));
 }
 
+int tq4_pack_bf16(const uint16_t *w_bf16, int64_t n, int64_t k, uint32_t sign_bits,
+                  uint8_t *packed, int32_t *nonfinite_count, void *stream) {
+  if (n < 0 || k < 0 || k % 32 != 0) return TQ4_E_SHAPE;
+  if (n == 0 || k == 0) return TQ4_OK;
+  if (w_bf16 == nullptr || packed == nullptr) return TQ4_E_NULL;
+  if (!aligned(w_bf16, 16) || !aligned(packed, 4) ||
+      (nonfinite_count != nullptr && !aligned(nonfinite_count, 4)))
+    return TQ4_E_ALIGN;
+  return device_status(tq4::launch_pack_bf16(w_bf16, n * (k / 32), sign_bits, packed,
+                                             nonfinite_count, as_stream(stream)));
+}
+
 int tq4_act_rht(const uint16_t *x_bf16, int64_t m, int64_t k, uint32_t sign_bits,
                 uint16_t *xt_f16, void *stream) {
   if (m < 0 || k < 0 || k % 32 != 0) return TQ4_E_SHAPE;

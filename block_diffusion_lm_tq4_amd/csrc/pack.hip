@@ -26,28 +26,50 @@ struct PackArgs {
   Codebook cb;
 };
 
-__global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, int64_t n_blocks,
+// The block's 32 weights as fp32 values (every bf16 value is exact in fp32).
+__device__ inline void load_weights(const float *w, float (&e)[32]) {
+  const float4 *src = reinterpret_cast<const float4 *>(w);  // 128 contiguous bytes
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 q = src[i];
+    e[4 * i] = q.x;
+    e[4 * i + 1] = q.y;
+    e[4 * i + 2] = q.z;
+    e[4 * i + 3] = q.w;
+  }
+}
+
+__device__ inline void load_weights(const uint16_t *w, float (&e)[32]) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(w);  // 64 contiguous bytes
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 q = src[i];
+    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
+      e[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <typename In>
+__global__ __launch_bounds__(256) void pack_kernel(const In *__restrict__ w, int64_t n_blocks,
                                                    uint32_t sign_bits, PackArgs args,
                                                    uint8_t *__restrict__ packed,
                                                    int32_t *__restrict__ nonfinite) {
   const int64_t blk = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (blk >= n_blocks) return;
 
-  // 32 fp32 weights, 128 contiguous bytes.
-  const float4 *src = reinterpret_cast<const float4 *>(w + blk * 32);
+  float e[32];
+  load_weights(w + blk * 32, e);
   double v[32];
   bool finite = true;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 q = src[i];
-    const float e[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = 4 * i + j;
-      finite = finite && isfinite(e[j]);
-      const double d = static_cast<double>(e[j]);
-      v[idx] = ((sign_bits >> idx) & 1u) ? -d : d;
-    }
+  for (int idx = 0; idx < 32; ++idx) {
+    finite = finite && isfinite(e[idx]);
+    const double d = static_cast<double>(e[idx]);
+    v[idx] = ((sign_bits >> idx) & 1u) ? -d : d;
   }
 
   // Walsh-Hadamard transform, natural (Sylvester) order.
@@ -115,16 +137,29 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, 
 
 }  // namespace
 
-hipError_t launch_pack(const float *w, int64_t n_blocks, uint32_t sign_bits, uint8_t *packed,
-                       int32_t *nonfinite, hipStream_t s) {
+namespace {
+template <typename In>
+hipError_t launch_pack_t(const In *w, int64_t n_blocks, uint32_t sign_bits, uint8_t *packed,
+                         int32_t *nonfinite, hipStream_t s) {
   if (n_blocks == 0) return hipSuccess;
   PackArgs args;
   args.cb = codebook();
   const int threads = 256;
   const int64_t grid = (n_blocks + threads - 1) / threads;
-  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(grid)), dim3(threads), 0, s, w,
+  hipLaunchKernelGGL(pack_kernel<In>, dim3(static_cast<unsigned>(grid)), dim3(threads), 0, s, w,
                      n_blocks, sign_bits, args, packed, nonfinite);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_pack(const float *w, int64_t n_blocks, uint32_t sign_bits, uint8_t *packed,
+                       int32_t *nonfinite, hipStream_t s) {
+  return launch_pack_t(w, n_blocks, sign_bits, packed, nonfinite, s);
+}
+
+hipError_t launch_pack_bf16(const uint16_t *w, int64_t n_blocks, uint32_t sign_bits,
+                            uint8_t *packed, int32_t *nonfinite, hipStream_t s) {
+  return launch_pack_t(w, n_blocks, sign_bits, packed, nonfinite, s);
 }
 
 }  // namespace tq4

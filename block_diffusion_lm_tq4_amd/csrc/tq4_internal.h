@@ -65,6 +65,8 @@ __device__ inline void rotate_block_bf16(const uint16_t *x, uint32_t sign_bits, 
 // ---- launchers (return hipSuccess or the launch error) --------------------
 hipError_t launch_pack(const float *w, int64_t n_blocks, uint32_t sign_bits,
                        uint8_t *packed, int32_t *nonfinite, hipStream_t s);
+hipError_t launch_pack_bf16(const uint16_t *w, int64_t n_blocks, uint32_t sign_bits,
+                            uint8_t *packed, int32_t *nonfinite, hipStream_t s);
 
 // Rotate [m, k] bf16 rows to fp16.
 hipError_t launch_act_rht_bf16(const uint16_t *x, int64_t m, int64_t k, uint32_t sign_bits,

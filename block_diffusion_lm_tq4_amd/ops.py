@@ -63,16 +63,22 @@ def packed_size(n: int, k: int) -> int:
     return int(lib().tq4_packed_size(n, k))
 
 
-def pack(w: torch.Tensor, sign_bits: int, nonfinite: torch.Tensor | None = None) -> torch.Tensor:
-    """fp32 W [n, k] -> packed uint8 [n, k/32, 20] (tq4_pack)."""
-    _cuda_contig(w, "w", torch.float32)
+def pack(w: torch.Tensor, sign_bits: int, nonfinite: torch.Tensor | None = None,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 or bf16 W [n, k] -> packed uint8 [n, k/32, 20] (tq4_pack / tq4_pack_bf16)."""
+    _require(w.dtype in (torch.float32, torch.bfloat16), "w must be fp32 or bf16")
+    _cuda_contig(w, "w", w.dtype)
     _require(w.dim() == 2 and w.shape[1] % BLOCK == 0, "w must be [n, k] with k % 32 == 0")
     n, k = w.shape
-    out = torch.empty((n, k // BLOCK, BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    if out is None:
+        out = torch.empty((n, k // BLOCK, BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    _cuda_contig(out, "out", torch.uint8)
+    _require(out.numel() == n * (k // BLOCK) * BLOCK_BYTES, "out must hold n * k/32 * 20 bytes")
     if nonfinite is not None:
         _cuda_contig(nonfinite, "nonfinite", torch.int32)
-    check("tq4_pack", lib().tq4_pack(w.data_ptr(), n, k, sign_bits & 0xFFFFFFFF, out.data_ptr(),
-                                     _ptr(nonfinite), _stream(w.device)))
+    fn = "tq4_pack" if w.dtype == torch.float32 else "tq4_pack_bf16"
+    check(fn, getattr(lib(), fn)(w.data_ptr(), n, k, sign_bits & 0xFFFFFFFF, out.data_ptr(),
+                                 _ptr(nonfinite), _stream(w.device)))
     return out
 
 

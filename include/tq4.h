@@ -83,6 +83,14 @@ size_t tq4_packed_size(int64_t n, int64_t k);
 int tq4_pack(const float *w, int64_t n, int64_t k, uint32_t sign_bits,
              uint8_t *packed, int32_t *nonfinite_count, void *stream);
 
+/* tq4_pack for BF16 weights (the form the checkpoint ships in; model card,
+ * Reproduction: quantizing both BF16 towers): w_bf16 is [n, k] bf16 bit
+ * patterns, row-major, device, 16-byte aligned.  Every bf16 value is exact in
+ * fp32, so the result is byte-identical to tq4_pack on the same values
+ * widened to fp32.  Other arguments and errors as tq4_pack. */
+int tq4_pack_bf16(const uint16_t *w_bf16, int64_t n, int64_t k, uint32_t sign_bits,
+                  uint8_t *packed, int32_t *nonfinite_count, void *stream);
+
 /* Rotate activations per 32-block: xt[m, :] = R x[m, :] with
  * R = H32 diag(s) / sqrt(32) on each block, fp32 arithmetic, result rounded to
  * fp16.  x: bf16 bit patterns [m, k] (device, 16-byte aligned); xt: fp16 bit

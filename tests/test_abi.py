@@ -74,6 +74,16 @@ def test_pack_argument_errors(L):
     assert L.tq4_pack(None, 0, 32, 0, None, None, None) == OK      # empty: no-op
 
 
+def test_pack_bf16_argument_errors(L):
+    assert L.tq4_pack_bf16(FAKE, 4, 33, 0, FAKE, None, None) == E_SHAPE
+    assert L.tq4_pack_bf16(FAKE, -1, 32, 0, FAKE, None, None) == E_SHAPE
+    assert L.tq4_pack_bf16(FAKE, 0, 32, 0, None, None, None) == OK
+    assert L.tq4_pack_bf16(None, 4, 32, 0, FAKE, None, None) == E_NULL
+    assert L.tq4_pack_bf16(FAKE, 4, 32, 0, None, None, None) == E_NULL
+    assert L.tq4_pack_bf16(FAKE + 8, 4, 32, 0, FAKE, None, None) == E_ALIGN
+    assert L.tq4_pack_bf16(FAKE, 4, 32, 0, FAKE + 2, None, None) == E_ALIGN
+
+
 def test_act_rht_argument_errors(L):
     assert L.tq4_act_rht(FAKE, 4, 40, 0, FAKE, None) == E_SHAPE
     assert L.tq4_act_rht(None, 4, 32, 0, FAKE, None) == E_NULL

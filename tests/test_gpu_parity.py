@@ -74,6 +74,24 @@ def test_pack_moe_experts_equal_oracle(experts):
     assert mismatched == []
 
 
+@pytest.mark.parametrize("n,k,kind", [
+    (8192, 2688, "gaussian"),        # dense denoiser projection, from bf16
+    (1856, 2688, "student_t3"),      # an expert's up projection, heavy-tailed
+    (37, 96, "gaussian"),
+])
+def test_pack_bf16_equals_oracle(dev, n, k, kind):
+    # the checkpoint's bf16 weights: the oracle packs the same values widened
+    # to fp32 (exact), so the bytes must agree
+    w = I.weights(n, k, kind)
+    w_bits = O.bf16_bits_from_f32(w)
+    w_bf = O.f64_from_bf16_bits(w_bits).astype(np.float32)
+    p = _ops().pack(_bf16(w_bits, dev), SB).cpu().numpy()
+    assert np.array_equal(p, O.pack(w_bf, SB))
+    # and tq4_pack on the widened values gives the same bytes
+    p32 = _ops().pack(torch.from_numpy(w_bf).to(dev), SB).cpu().numpy()
+    assert np.array_equal(p, p32)
+
+
 def test_pack_special_blocks(dev):
     w = np.zeros((6, 64), dtype=np.float32)
     w[1, 7] = 1.0                                   # one-hot block
