@@ -297,8 +297,9 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
 // its weights (32 rows x 80 bytes).
 //
 //  * kDmaProducers waves keep the loads going: producer p takes chunks p,
-//    p + kDmaProducers, ..., keeps up to three of them in flight, and as each
-//    lands (its loads retire in issue order) raises that chunk's LDS flag.
+//    p + kDmaProducers, ..., keeps three of them in flight, and as each lands
+//    (its loads retire in issue order) raises that chunk's LDS flag and
+//    issues the chunk three ahead.
 //  * kDmaConsumers waves take chunks round robin; each waits for the chunk's
 //    flag, rotates the x blocks (two bf16 MFMAs per block against the +-1
 //    matrix, as in skinny_kernel), decodes its lane's code words through the
@@ -364,24 +365,26 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
     const uint32_t flag_addr = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint32_t *)ready));
     // the first chunk goes out before the barrier that publishes the cleared
-    // flags and the pair table; then up to three chunks stay in flight
+    // flags and the pair table; then three of this producer's chunks stay in
+    // flight: as each lands it is flagged and the chunk three ahead is issued
     if (p < chunks) issue(p);
     __builtin_amdgcn_s_barrier();
+    for (int i = 1; i < 3; ++i)
+      if (p + i * kDmaProducers < chunks) issue(p + i * kDmaProducers);
     for (int c = p; c < chunks; c += kDmaProducers) {
-      const bool more1 = c + kDmaProducers < chunks;
-      const bool more2 = c + 2 * kDmaProducers < chunks;
-      if (c == p && more1) issue(c + kDmaProducers);
-      if (more2) issue(c + 2 * kDmaProducers);
-      // loads of chunk c are in once only the later chunks' are outstanding
-      if (more2)
+      // loads of chunk c are in once only the later chunks' (7 loads each)
+      // are outstanding
+      const int later = (c + kDmaProducers < chunks) + (c + 2 * kDmaProducers < chunks);
+      if (later == 2)
         __builtin_amdgcn_s_waitcnt(0x0F7E);  // vmcnt(14)
-      else if (more1)
+      else if (later == 1)
         __builtin_amdgcn_s_waitcnt(0x0F77);  // vmcnt(7)
       else
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       // (written in asm: the compiler cannot tell this flag from the slots
       // still being filled and would wait for every load in flight first)
       asm volatile("ds_write_b32 %0, %1" ::"v"(flag_addr + 4 * c), "v"(1u) : "memory");
+      if (c + 3 * kDmaProducers < chunks) issue(c + 3 * kDmaProducers);
     }
     __syncthreads();  // all chunks consumed
     __syncthreads();  // partial sums in LDS
