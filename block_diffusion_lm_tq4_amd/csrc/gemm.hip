@@ -102,8 +102,15 @@ struct WRaw {
 // LUTC copies of the pair table are interleaved (entry e of copy q at
 // e * LUTC + q; lane L uses copy L % LUTC), so that random lookups by the
 // lanes of a wave spread over the LDS banks.
+// Occupancy targets (waves per SIMD) for the tile heights the MoE layer
+// uses: more resident workgroups hide the per-chunk load latency better than
+// the registers the compiler would otherwise spend (measured on the MoE
+// layer at 16 and 1024 tokens).
+constexpr int waves_per_eu_for(int msub) { return msub == 1 ? 6 : (msub == 4 ? 4 : 1); }
+
 template <int MSUB, int NSUB, int LUTC, int MODE>
-__global__ __launch_bounds__(64 * kWaves) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(64 * kWaves)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(GemmArgs g) {
   constexpr int TM = 16 * MSUB;           // activation rows per workgroup
   constexpr int TN = 16 * NSUB * kWaves;  // weight rows per workgroup
 
