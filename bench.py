@@ -10,7 +10,9 @@ its weights from HBM.  Inputs are resident in HBM before timing starts.
 
 Extra legs in the same JSON line: the M=4096 prefill projection (TFLOP/s,
 Student-t weights) and the 128-expert top-6 MoE layer at 16 and 1024 tokens
-(uniform and Zipf routing), each timed the same way, with its own roofline.
+(uniform and Zipf routing), each timed the same way, with its own roofline;
+the offline quantizer's throughput; and the fused bias + residual tail
+(tq4_linear_epilogue) at M=16 and M=4096 against the plain call.
 
 `roofline` is for the dominant kernel of the headline step: at M=16 the whole
 tq4_linear call is one kernel (rotation fused), so its time per launch is the
@@ -181,6 +183,40 @@ def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb):
                 flops=2.0 * pairs * 2 * wl.n1 * wl.k, experts_touched=int(touched))
 
 
+def epilogue_leg(torch, np, ops, I, wl, steps, warmup, copies, dev, sb):
+    """The fused bias + residual tail (tq4_linear_epilogue, the residual being
+    the output itself, as in a residual stream) against the same call without
+    a tail and against that call followed by the two adds as torch kernels."""
+    w = I.weights(wl.n, wl.k, wl.weights)
+    packed = ops.pack(torch.from_numpy(w).to(dev), sb)
+    del w
+    stack = [packed] + [packed.clone() for _ in range(copies - 1)]
+    x = bf16_dev(torch, np, I.activations_bf16(wl.m, wl.k), dev)
+    y = torch.zeros((wl.m, wl.n), dtype=torch.float32, device=dev)
+    t = torch.empty_like(y)
+    bias = torch.randn(wl.n, dtype=torch.float32, device=dev)
+    ws = torch.zeros(ops.linear_workspace_size(wl.m, wl.k, wl.n), dtype=torch.uint8, device=dev)
+
+    def fused(i):
+        ops.linear_epilogue(x, stack[i % copies], sb, bias=bias, residual=y, out=y, workspace=ws)
+
+    def plain(i):
+        ops.linear(x, stack[i % copies], sb, out=t, workspace=ws)
+
+    def unfused(i):
+        plain(i)
+        t.add_(bias)
+        y.add_(t)
+
+    ms_f = time_loop(torch, fused, steps, warmup)
+    ms_p = time_loop(torch, plain, steps, warmup)
+    ms_u = time_loop(torch, unfused, steps, warmup)
+    return {"shape": f"{wl.m}x{wl.k}x{wl.n}", "fused_us": round(ms_f * 1e3, 2),
+            "no_tail_us": round(ms_p * 1e3, 2), "linear_then_torch_adds_us": round(ms_u * 1e3, 2),
+            "tail_cost_us": round((ms_f - ms_p) * 1e3, 2),
+            "tail_bytes": wl.m * wl.n * 4 + wl.n * 4}
+
+
 def pack_leg(torch, np, ops, I, steps, warmup, dev, sb, n=8192, k=2688):
     """Offline quantizer throughput (tq4_pack_bf16 and tq4_pack) on one
     denoiser-projection-sized matrix, weights resident on the device."""
@@ -237,7 +273,7 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=48)
     ap.add_argument("--legs", default="all",
                     help="all | none | comma list of dense_m4096_t3,moe_t16,"
-                         "moe_t1024_uniform,moe_t1024_zipf,pack")
+                         "moe_t1024_uniform,moe_t1024_zipf,pack,epilogue")
     ap.add_argument("--only", default=None,
                     help="profile helper: run just this workload (no JSON contract)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -302,13 +338,25 @@ def main() -> int:
 
     legs = {}
     names = ([] if args.legs == "none" else
-             ["dense_m4096_t3", "moe_t16", "moe_t1024_uniform", "moe_t1024_zipf", "pack"]
+             ["dense_m4096_t3", "moe_t16", "moe_t1024_uniform", "moe_t1024_zipf", "pack",
+              "epilogue"]
              if args.legs == "all" else args.legs.split(","))
     experts = None
     for name in names:
         if name == "pack":
             log("pack: running")
             legs[name] = pack_leg(torch, np, ops, I, max(5, args.steps // 20), 2, dev, sb)
+            log(name, json.dumps(legs[name]))
+            continue
+        if name == "epilogue":
+            log("epilogue: running")
+            legs[name] = {
+                "dense_m16": epilogue_leg(torch, np, ops, I, I.WORKLOADS["dense_m16"],
+                                          max(5, args.steps // 2), max(2, args.warmup // 2),
+                                          args.copies, dev, sb),
+                "dense_m4096_t3": epilogue_leg(torch, np, ops, I, I.WORKLOADS["dense_m4096_t3"],
+                                               max(5, args.steps // 20),
+                                               max(2, args.warmup // 10), 2, dev, sb)}
             log(name, json.dumps(legs[name]))
             continue
         wl2 = I.WORKLOADS[name]

@@ -53,6 +53,8 @@ struct GemmArgs {
   float *out;                // output rows, stride n
   uint16_t *out16;           // MoE up: rotated hidden rows (fp16 bits), stride n
   float *partial;            // [ksplit][m][n] (dense split-K)
+  const float *bias;         // dense: [n] or null
+  const float *residual;     // dense: [m][n] or null (may equal out)
   const int32_t *perm;       // MoE: bucket position -> pair
   const MoETile *tiles;      // MoE tile list
   const int32_t *n_tiles;    // MoE tile count (device)
@@ -85,6 +87,80 @@ __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *l
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
+}
+
+// Stores a wave's MS x NS grid of 16x16 fp32 accumulator tiles of a dense
+// product, plus the tail: lane (grp, r) holds, in tile (i, j), the rows
+// m0 + 16 i + 4 grp + v (v = 0..3) of column n0 + 16 j + r; out has row
+// stride nlim.  Per batch of two row tiles, every residual value is loaded and
+// every sum formed before the first store, so the loads overlap and no store
+// waits on memory.  The residual may be the output itself, which keeps the
+// compiler from moving a load above an earlier store; reordering by hand is
+// sound because each element is read and written by its own lane only.
+// kCheck = false: the whole grid lies inside the output (no bounds tests).
+template <bool kCheck, int MS, int NS>
+__device__ inline void store_tiles_impl(const floatx4 (&acc)[MS][NS], float *out,
+                                        const float *bias, const float *residual, int64_t m0,
+                                        int64_t n0, int64_t mlim, int64_t nlim, int grp, int r) {
+  float bv[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int64_t n = n0 + 16 * j + r;
+    bv[j] = (bias != nullptr && (!kCheck || n < nlim)) ? bias[n] : 0.f;
+  }
+  constexpr int kIB = 2;  // row tiles per batch
+#pragma unroll
+  for (int i0 = 0; i0 < MS; i0 += kIB) {
+    float yv[kIB][NS][4];
+    if (residual != nullptr) {
+#pragma unroll
+      for (int ii = 0; ii < kIB; ++ii)
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int64_t m = m0 + 16 * (i0 + ii) + 4 * grp + v;
+            const int64_t n = n0 + 16 * j + r;
+            const bool in = i0 + ii < MS && (!kCheck || (m < mlim && n < nlim));
+            yv[ii][j][v] = in ? residual[m * nlim + n] : 0.f;
+          }
+    }
+#pragma unroll
+    for (int ii = 0; ii < kIB; ++ii) {
+      if (i0 + ii >= MS) break;
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float y = acc[i0 + ii][j][v];
+          if (bias != nullptr) y += bv[j];
+          if (residual != nullptr) y += yv[ii][j][v];
+          yv[ii][j][v] = y;
+        }
+    }
+#pragma unroll
+    for (int ii = 0; ii < kIB; ++ii) {
+      if (i0 + ii >= MS) break;
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t m = m0 + 16 * (i0 + ii) + 4 * grp + v;
+          const int64_t n = n0 + 16 * j + r;
+          if (!kCheck || (m < mlim && n < nlim)) out[m * nlim + n] = yv[ii][j][v];
+        }
+    }
+  }
+}
+
+template <int MS, int NS>
+__device__ inline void store_tiles(const floatx4 (&acc)[MS][NS], float *out, const float *bias,
+                                   const float *residual, int64_t m0, int64_t n0, int64_t mlim,
+                                   int64_t nlim, int grp, int r) {
+  if (m0 + 16 * MS <= mlim && n0 + 16 * NS <= nlim)
+    store_tiles_impl<false>(acc, out, bias, residual, m0, n0, mlim, nlim, grp, r);
+  else
+    store_tiles_impl<true>(acc, out, bias, residual, m0, n0, mlim, nlim, grp, r);
 }
 
 __device__ inline half2v scale_pair(uint32_t bf16_bits) {
@@ -284,18 +360,11 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
 
   // ---- epilogue: lane holds C[4*grp + v][r] of every 16x16 tile ----------
   if constexpr (MODE == kDense) {
-    float *dst = g.ksplit > 1 ? g.partial + static_cast<int64_t>(split) * g.m * g.n : g.out;
-#pragma unroll
-    for (int i = 0; i < MSUB; ++i)
-#pragma unroll
-      for (int j = 0; j < NSUB; ++j) {
-        const int64_t n = n_base + wave * (16 * NSUB) + 16 * j + r;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t m = m_base + 16 * i + 4 * grp + v;
-          if (m < g.m && n < g.n) dst[m * g.n + n] = acc[i][j][v];
-        }
-      }
+    // split-K partial sums take the tail in the reduction
+    const bool split_k = g.ksplit > 1;
+    float *dst = split_k ? g.partial + static_cast<int64_t>(split) * g.m * g.n : g.out;
+    store_tiles(acc, dst, split_k ? nullptr : g.bias, split_k ? nullptr : g.residual, m_base,
+                n_base + wave * (16 * NSUB), g.m, g.n, grp, r);
   } else if constexpr (MODE == kMoEUp) {
     // h = relu(u)^2, then its rotation ht = H32 diag(s) h / sqrt(32), stored
     // as fp16: a wave's 32 output columns are one 32-block of h (NSUB == 2).
@@ -604,17 +673,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_big_kernel(GemmArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding chunks' loads
 
-#pragma unroll
-  for (int i = 0; i < kBigMSub; ++i)
-#pragma unroll
-    for (int j = 0; j < kBigNSub; ++j) {
-      const int64_t n = n_base + wave * (16 * kBigNSub) + 16 * j + r;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = m_base + 16 * i + 4 * grp + v;
-        if (m < g.m && n < g.n) g.out[m * g.n + n] = acc[i][j][v];
-      }
-    }
+  store_tiles(acc, g.out, g.bias, g.residual, m_base, n_base + wave * (16 * kBigNSub), g.m, g.n,
+              grp, r);
 }
 
 // Dense large-M variant with two waves on every SIMD.  Tile: 256 activation
@@ -800,28 +860,20 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding chunks' loads
 
-#pragma unroll
-  for (int i = 0; i < kHugeMSub; ++i)
-#pragma unroll
-    for (int j = 0; j < kHugeNSub; ++j) {
-      const int64_t n = n_base + wn * (16 * kHugeNSub) + 16 * j + r;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = m_base + wm * (16 * kHugeMSub) + 16 * i + 4 * grp + v;
-        if (m < g.m && n < g.n) g.out[m * g.n + n] = acc[i][j][v];
-      }
-    }
+  store_tiles(acc, g.out, g.bias, g.residual, m_base + wm * (16 * kHugeMSub),
+              n_base + wn * (16 * kHugeNSub), g.m, g.n, grp, r);
 }
 
-// y[i] = sum over splits of partial[s][i], in split order.
+// y[i] = sum over splits of partial[s][i], in split order, then the tail.
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ partial,
-                                                              int32_t ksplit, int64_t mn,
-                                                              float *__restrict__ y) {
+                                                              int32_t ksplit, int64_t m, int64_t n,
+                                                              Tail tail, float *y) {
+  const int64_t mn = m * n;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= mn) return;
   float s = partial[i];
   for (int q = 1; q < ksplit; ++q) s += partial[q * mn + i];
-  y[i] = s;
+  y[i] = add_tail(s, tail.bias, tail.residual, i / n, i % n, n);
 }
 
 template <int MSUB, int NSUB, int LUTC, int MODE>
@@ -898,12 +950,14 @@ DensePlan plan_dense(int64_t m, int64_t k, int64_t n) {
 
 hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64_t k,
                         const uint8_t *packed, int64_t n, float *y, float *partial,
-                        hipStream_t s) {
+                        hipStream_t s, const Tail &tail) {
   GemmArgs g{};
   g.a = xt;
   g.w = packed;
   g.out = y;
   g.partial = partial;
+  g.bias = tail.bias;
+  g.residual = tail.residual;
   g.m = m;
   g.n = n;
   g.k = k;
@@ -917,7 +971,7 @@ hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64
   if (e != hipSuccess || p.ksplit == 1) return e;
   const int64_t mn = m * n;
   hipLaunchKernelGGL(reduce_partials_kernel, dim3(static_cast<unsigned>((mn + 255) / 256)),
-                     dim3(256), 0, s, partial, p.ksplit, mn, y);
+                     dim3(256), 0, s, partial, p.ksplit, m, n, tail, y);
   return hipGetLastError();
 }
 

@@ -35,7 +35,21 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
   if (i < count) p[i] = 0.f;
 }
 
+// y = bias + residual, for a product with an empty k.
+__global__ __launch_bounds__(256) void tail_only_kernel(Tail t, int64_t m, int64_t n, float *y) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < m * n) y[i] = add_tail(0.f, t.bias, t.residual, i / n, i % n, n);
+}
+
 }  // namespace
+
+hipError_t launch_tail_only(const Tail &t, int64_t m, int64_t n, float *y, hipStream_t s) {
+  const int64_t count = m * n;
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(tail_only_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256),
+                     0, s, t, m, n, y);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s) {
   if (count == 0) return hipSuccess;

@@ -63,6 +63,8 @@ struct SkinnyArgs {
   const uint16_t *x;  // bf16 [m][k]
   const uint8_t *w;   // packed [n][k/32][20]
   float *y;           // [m][n]
+  const float *bias;      // [n] or null
+  const float *residual;  // [m][n] or null (may equal y)
   int32_t m, n, kb;   // kb = k / 32
   uint32_t sign_bits;
   Codebook cb;
@@ -91,13 +93,6 @@ __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *l
 
 __device__ inline half2v scale_pair(uint32_t bf16_bits) {
   const float f = __uint_as_float(bf16_bits << 16);
-  return __builtin_convertvector((float2v){f, f}, half2v);
-}
-
-// the scale of half `h` (0: elements 0-15, 1: 16-31) of a block from its
-// scale word (S0 in the low 16 bits, S1 in the high 16 bits)
-__device__ inline half2v half_scale(uint32_t word, int h) {
-  const float f = __uint_as_float((word << (16 - 16 * h)) & 0xFFFF0000u);
   return __builtin_convertvector((float2v){f, f}, half2v);
 }
 
@@ -279,7 +274,9 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * grp + v;
-        if (m < g.m) g.y[static_cast<int64_t>(m) * g.n + n] = s[v] * rs32;
+        if (m < g.m)
+          g.y[static_cast<int64_t>(m) * g.n + n] =
+              add_tail(s[v] * rs32, g.bias, g.residual, m, n, g.n);
       }
     }
   }
@@ -503,7 +500,9 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
     for (int w = 1; w < kDmaConsumers; ++w) sum += red[((w * kRowTiles + j) * 4 + v) * 64 + lane];
     const int n = n0 + r + 16 * j;
     const int m = 4 * grp + v;
-    if (n < g.n && m < g.m) g.y[static_cast<int64_t>(m) * g.n + n] = sum * 0x1.6a09e6p-3f;
+    if (n < g.n && m < g.m)
+      g.y[static_cast<int64_t>(m) * g.n + n] =
+          add_tail(sum * 0x1.6a09e6p-3f, g.bias, g.residual, m, n, g.n);
   }
 }
 
@@ -538,11 +537,14 @@ bool skinny_fits(int64_t m, int64_t k, int64_t n) {
 }
 
 hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
-                         int64_t n, uint32_t sign_bits, float *y, hipStream_t s) {
+                         int64_t n, uint32_t sign_bits, float *y, hipStream_t s,
+                         const Tail &tail) {
   SkinnyArgs a{};
   a.x = x;
   a.w = packed;
   a.y = y;
+  a.bias = tail.bias;
+  a.residual = tail.residual;
   a.m = static_cast<int32_t>(m);
   a.n = static_cast<int32_t>(n);
   a.kb = static_cast<int32_t>(k / 32);

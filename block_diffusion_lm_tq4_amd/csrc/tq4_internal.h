@@ -62,6 +62,24 @@ __device__ inline void rotate_block_bf16(const uint16_t *x, uint32_t sign_bits, 
   }
 }
 
+// The linear layer's additive tail on one output element: acc + bias[n] +
+// residual[m, n] (either pointer may be null), in that order, fp32.  No
+// contraction: the first add is never fused with the product's last multiply,
+// so the result is the rounded product plus the tail, as two separate adds.
+__device__ inline float add_tail(float acc, const float *bias, const float *residual, int64_t m,
+                                 int64_t n, int64_t ldn) {
+#pragma clang fp contract(off)
+  if (bias != nullptr) acc += bias[n];
+  if (residual != nullptr) acc += residual[m * ldn + n];
+  return acc;
+}
+
+// Bias and residual of a dense product (both may be null).
+struct Tail {
+  const float *bias;      // [n]
+  const float *residual;  // [m, n], may equal y
+};
+
 // ---- launchers (return hipSuccess or the launch error) --------------------
 hipError_t launch_pack(const float *w, int64_t n_blocks, uint32_t sign_bits,
                        uint8_t *packed, int32_t *nonfinite, hipStream_t s);
@@ -73,6 +91,9 @@ hipError_t launch_act_rht_bf16(const uint16_t *x, int64_t m, int64_t k, uint32_t
                                uint16_t *xt, hipStream_t s);
 
 hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s);
+
+// y[i] = bias[i % n] + residual[i] over an [m, n] output (k == 0 products).
+hipError_t launch_tail_only(const Tail &t, int64_t m, int64_t n, float *y, hipStream_t s);
 
 // Dense product y[m, n] = xt[m, :] . Zhat[n, :]^T with xt already rotated.
 struct DensePlan {
@@ -87,12 +108,13 @@ struct DensePlan {
 DensePlan plan_dense(int64_t m, int64_t k, int64_t n);
 hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64_t k,
                         const uint8_t *packed, int64_t n, float *y, float *partial,
-                        hipStream_t s);
+                        hipStream_t s, const Tail &tail = Tail{});
 
 // Single-kernel path for m <= 16 (rotation fused, no workspace).
 bool skinny_fits(int64_t m, int64_t k, int64_t n);
 hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
-                         int64_t n, uint32_t sign_bits, float *y, hipStream_t s);
+                         int64_t n, uint32_t sign_bits, float *y, hipStream_t s,
+                         const Tail &tail = Tail{});
 
 // MoE pieces.
 struct MoETile {  // one m-tile of one expert's segment in bucket order

@@ -134,6 +134,25 @@ int tq4_linear_rotated(const uint16_t *xt_f16, int64_t m, int64_t k,
                        const uint8_t *packed, int64_t n, float *y, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* tq4_linear with the layer's additive tail fused into the product's final
+ * store: y[m, n] = sum_k x[m, k] * W_hat[n, k] + bias[n] + residual[m, n], in
+ * fp32 (the product, then + bias, then + residual).  The quantized Linear
+ * modules of the model card (section Running it) replace nn.Linear, whose
+ * optional bias this is; the residual add is the sum every block of the
+ * layer stack feeds into.
+ *   bias     : [n] fp32, device, 4-byte aligned, or NULL (no bias)
+ *   residual : [m, n] fp32, device, 4-byte aligned, or NULL (no residual);
+ *              it may be y itself (each element is read before it is
+ *              written, by the same thread), but must not otherwise overlap y
+ * Everything else (arguments, workspace, errors, determinism) as tq4_linear,
+ * plus TQ4_E_SHAPE for a residual that overlaps y without being y.  With both
+ * NULL the result equals tq4_linear's bit for bit.  k == 0 writes bias +
+ * residual. */
+int tq4_linear_epilogue(const uint16_t *x_bf16, int64_t m, int64_t k,
+                        const uint8_t *packed, int64_t n, uint32_t sign_bits,
+                        const float *bias, const float *residual, float *y,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /* Stable bucketing of the t*topk (token, slot) pairs by expert, the routing
  * step of the sync-free MoE (model card, Running it; 128 experts, top-6 in
  * The model underneath).  Pair p = token * topk + slot.

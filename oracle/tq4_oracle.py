@@ -64,6 +64,7 @@ __all__ = [
     "dequant_rotated",
     "dequant",
     "linear",
+    "linear_epilogue",
     "moe",
     "bucket_pairs",
     "router",
@@ -296,6 +297,23 @@ def linear(x_bf16: np.ndarray, packed: np.ndarray, sign_bits: int) -> np.ndarray
     """y = x . W_hat^T in fp64; x is given as bf16 bit patterns [M, K]."""
     x = f64_from_bf16_bits(x_bf16)
     return x @ dequant(packed, sign_bits).T
+
+
+def linear_epilogue(x_bf16: np.ndarray, packed: np.ndarray, sign_bits: int,
+                    bias: np.ndarray | None = None,
+                    residual: np.ndarray | None = None) -> np.ndarray:
+    """y = x . W_hat^T + bias[n] + residual[m, n] in fp64, each term optional.
+
+    The model card (section Running it) swaps the model's quantized Linear
+    modules for an on-the-fly dequantizing layer; a Linear's optional bias is
+    added per output feature, and the block's residual stream is added per
+    element.  Terms are summed left to right: product, bias, residual."""
+    y = linear(x_bf16, packed, sign_bits)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    if residual is not None:
+        y = y + np.asarray(residual, dtype=np.float64)
+    return y
 
 
 def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,

@@ -116,6 +116,32 @@ def test_linear_argument_errors(L):
     assert call(m=0) == OK and call(n=0) == OK      # empty output: no-op
 
 
+def test_linear_epilogue_argument_errors(L):
+    ws = L.tq4_linear_workspace_size(100, 2688, 8192)
+    y = FAKE
+    args = dict(x=FAKE, m=100, k=2688, p=FAKE, n=8192, sb=0, b=FAKE, r=FAKE + (1 << 24), y=y,
+                ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.tq4_linear_epilogue(a["x"], a["m"], a["k"], a["p"], a["n"], a["sb"], a["b"],
+                                     a["r"], a["y"], a["ws"], a["wsb"], None)
+
+    assert call(k=2690) == E_SHAPE
+    assert call(x=None) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(b=FAKE + 2) == E_ALIGN
+    assert call(r=FAKE + (1 << 24) + 2) == E_ALIGN
+    # a residual that overlaps y without being y (y spans 100 * 8192 * 4 bytes)
+    assert call(r=y + 4) == E_SHAPE
+    assert call(r=y + 100 * 8192 * 4 - 4) == E_SHAPE
+    assert call(ws=None) == E_WS                     # r == y and disjoint r are accepted
+    assert call(r=y, ws=None) == E_WS
+    assert call(r=y + 100 * 8192 * 4, ws=None) == E_WS
+    assert call(b=None, r=None, ws=None) == E_WS
+    assert call(m=0) == OK and call(n=0) == OK
+
+
 def test_moe_argument_errors(L):
     ws = L.tq4_moe_workspace_size(16, 6, 128, 1856, 2688)
     assert ws > 0

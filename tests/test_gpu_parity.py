@@ -253,6 +253,72 @@ def test_linear_rotated_equals_linear(dev, m, k, n):
         _check_close(b.cpu().numpy(), ref, "rotated")
 
 
+@pytest.mark.parametrize("m,k,n,tail", [
+    (16, 2688, 8192, "both"),      # M <= 16, LDS-direct kernel
+    (16, 256, 512, "residual"),
+    (5, 96, 17, "both"),           # M <= 16, register-load kernel
+    (7, 3072, 64, "bias"),
+    (33, 2688, 100, "both"),       # split-K: the tail rides the reduction
+    (300, 512, 520, "both"),
+    (64, 256, 32768, "bias"),      # one split, 64-row tiles
+    (512, 256, 16384, "both"),     # 128 x 256 tiles
+    (512, 128, 32768, "both"),     # 256 x 256 tiles
+    (129, 96, 33, "inplace"),      # residual is the output itself
+    (16, 2688, 8192, "inplace"),
+])
+def test_linear_epilogue_matches_oracle(dev, m, k, n, tail):
+    w = I.weights(n, k, seed=m + n)
+    x = I.activations_bf16(m, k, seed=5)
+    p_ref = O.pack(w, SB)
+    p_gpu = _ops().pack(torch.from_numpy(w).to(dev), SB)
+    ref0 = O.linear(x, p_ref, SB)
+    scale = float(np.sqrt(np.mean(ref0 * ref0)))
+    rng = np.random.default_rng(m * 31 + n)
+    bias = (rng.standard_normal(n) * scale).astype(np.float32)
+    res = (rng.standard_normal((m, n)) * scale).astype(np.float32)
+    use_b = tail in ("both", "bias", "inplace")
+    use_r = tail in ("both", "residual", "inplace")
+    xb = _bf16(x, dev)
+    b_d = torch.from_numpy(bias).to(dev) if use_b else None
+    r_d = torch.from_numpy(res).to(dev) if use_r else None
+    if tail == "inplace":
+        y = r_d.clone()
+        out = _ops().linear_epilogue(xb, p_gpu, SB, bias=b_d, residual=y, out=y)
+        assert out.data_ptr() == y.data_ptr()
+    else:
+        y = _ops().linear_epilogue(xb, p_gpu, SB, bias=b_d, residual=r_d)
+    plain = _ops().linear(xb, p_gpu, SB)
+    torch.cuda.synchronize()
+    ref = O.linear_epilogue(x, p_ref, SB, bias if use_b else None, res if use_r else None)
+    _check_close(y.cpu().numpy(), ref, f"epilogue {tail} {m}x{k}x{n}")
+    # the fused tail is the plain product followed by two fp32 adds, bit for bit
+    want = plain.clone()
+    if use_b:
+        want += b_d
+    if use_r:
+        want += r_d
+    assert torch.equal(y, want)
+
+
+def test_linear_epilogue_without_tail_is_linear(dev):
+    w = I.weights(300, 2688, seed=9)
+    p = _ops().pack(torch.from_numpy(w).to(dev), SB)
+    for m in (16, 100):
+        x = _bf16(I.activations_bf16(m, 2688), dev)
+        assert torch.equal(_ops().linear_epilogue(x, p, SB), _ops().linear(x, p, SB))
+
+
+def test_linear_epilogue_k0_writes_the_tail(dev):
+    x = torch.empty((4, 0), dtype=torch.bfloat16, device=dev)
+    p = torch.empty((8, 0, 20), dtype=torch.uint8, device=dev)
+    b = torch.arange(8, dtype=torch.float32, device=dev)
+    r = torch.full((4, 8), 0.5, device=dev)
+    y = _ops().linear_epilogue(x, p, SB, bias=b, residual=r)
+    assert torch.equal(y, b[None, :] + r)
+    y = _ops().linear_epilogue(x, p, SB, bias=b)
+    assert torch.equal(y, b[None, :].expand(4, 8))
+
+
 def test_linear_k0_writes_zeros(dev):
     x = torch.empty((4, 0), dtype=torch.bfloat16, device=dev)
     p = torch.empty((8, 0, 20), dtype=torch.uint8, device=dev)

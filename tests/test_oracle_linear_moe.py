@@ -60,6 +60,35 @@ def test_identity_rows_read_back_the_weights():
     assert np.array_equal(y, O.dequant(p, SB).T)
 
 
+def test_linear_epilogue_brute_force_and_special_cases():
+    w = I.weights(24, 64)
+    x = I.activations_bf16(5, 64)
+    p = O.pack(w, SB)
+    rng = np.random.default_rng(3)
+    bias = rng.standard_normal(24).astype(np.float32)
+    res = rng.standard_normal((5, 24)).astype(np.float32)
+    y = O.linear_epilogue(x, p, SB, bias, res)
+    xf = O.f64_from_bf16_bits(x)
+    # element by element from the decoded blocks, bias by output feature,
+    # residual by (row, feature)
+    for m, n in [(0, 0), (4, 23), (2, 7), (3, 16)]:
+        acc = 0.0
+        for b in range(2):
+            wb = _explicit_weight(p[n, b])
+            acc += sum(xf[m, b * 32 + j] * wb[j] for j in range(32))
+        want = acc + float(bias[n]) + float(res[m, n])
+        assert abs(want - y[m, n]) <= 1e-12 * max(1.0, abs(want))
+    # zero activations leave exactly bias + residual; no tail leaves the product
+    zero = np.zeros_like(x)
+    yz = O.linear_epilogue(zero, p, SB, bias, res)
+    for m in range(5):
+        for n in range(24):
+            assert yz[m, n] == float(bias[n]) + float(res[m, n])
+    assert np.array_equal(O.linear_epilogue(x, p, SB), O.linear(x, p, SB))
+    assert np.array_equal(O.linear_epilogue(zero, p, SB, bias=bias), np.tile(bias, (5, 1)))
+    assert np.array_equal(O.linear_epilogue(zero, p, SB, residual=res), res.astype(np.float64))
+
+
 def test_activation_rotation_identity():
     """x . W_hat^T == (R x) . Z_hat^T per block (R orthogonal)."""
     w = I.weights(128, 256)
