@@ -186,7 +186,8 @@ def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb):
 def epilogue_leg(torch, np, ops, I, wl, steps, warmup, copies, dev, sb):
     """The fused bias + residual tail (tq4_linear_epilogue, the residual being
     the output itself, as in a residual stream) against the same call without
-    a tail and against that call followed by the two adds as torch kernels."""
+    a tail and against that call followed by the two adds as torch kernels;
+    and the bf16 residual stream form (tq4_linear_epilogue_bf16)."""
     w = I.weights(wl.n, wl.k, wl.weights)
     packed = ops.pack(torch.from_numpy(w).to(dev), sb)
     del w
@@ -208,13 +209,21 @@ def epilogue_leg(torch, np, ops, I, wl, steps, warmup, copies, dev, sb):
         t.add_(bias)
         y.add_(t)
 
+    y16 = torch.zeros((wl.m, wl.n), dtype=torch.bfloat16, device=dev)
+
+    def fused_bf16(i):
+        ops.linear_epilogue_bf16(x, stack[i % copies], sb, bias=bias, residual=y16, out=y16,
+                                 workspace=ws)
+
     ms_f = time_loop(torch, fused, steps, warmup)
     ms_p = time_loop(torch, plain, steps, warmup)
     ms_u = time_loop(torch, unfused, steps, warmup)
+    ms_h = time_loop(torch, fused_bf16, steps, warmup)
     return {"shape": f"{wl.m}x{wl.k}x{wl.n}", "fused_us": round(ms_f * 1e3, 2),
             "no_tail_us": round(ms_p * 1e3, 2), "linear_then_torch_adds_us": round(ms_u * 1e3, 2),
             "tail_cost_us": round((ms_f - ms_p) * 1e3, 2),
-            "tail_bytes": wl.m * wl.n * 4 + wl.n * 4}
+            "tail_bytes": wl.m * wl.n * 4 + wl.n * 4,
+            "fused_bf16_stream_us": round(ms_h * 1e3, 2)}
 
 
 def pack_leg(torch, np, ops, I, steps, warmup, dev, sb, n=8192, k=2688):

@@ -5,6 +5,6 @@ by ``block_diffusion_lm_tq4_amd.build``.  ``ops`` is the torch-facing binding;
 ``inputs`` holds the seeded synthetic workloads.
 """
 
-from .ops import (act_rht, codebook, linear, linear_epilogue, linear_rotated,  # noqa: F401
-                  linear_workspace_size, moe_grouped, moe_route, moe_router, moe_workspace_size,
-                  pack, packed_size)
+from .ops import (act_rht, codebook, linear, linear_epilogue, linear_epilogue_bf16,  # noqa: F401
+                  linear_rotated, linear_workspace_size, moe_grouped, moe_route, moe_router,
+                  moe_workspace_size, pack, packed_size)

@@ -40,6 +40,8 @@ SIGNATURES = {
     "tq4_linear": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _U32, _P, _P, _SZ, _P]),
     "tq4_linear_epilogue": (ctypes.c_int,
                             [_P, _I64, _I64, _P, _I64, _U32, _P, _P, _P, _P, _SZ, _P]),
+    "tq4_linear_epilogue_bf16": (ctypes.c_int,
+                                 [_P, _I64, _I64, _P, _I64, _U32, _P, _P, _P, _P, _SZ, _P]),
     "tq4_linear_rotated": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "tq4_moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
     "tq4_moe_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64]),

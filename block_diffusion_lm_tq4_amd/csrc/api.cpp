@@ -152,37 +152,40 @@ size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n) {
 namespace {
 
 int linear_impl(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed, int64_t n,
-                uint32_t sign_bits, const tq4::Tail &tail, float *y, void *workspace,
+                uint32_t sign_bits, const tq4::Tail &tail, void *y, void *workspace,
                 size_t workspace_bytes, void *stream) {
   if (m < 0 || k < 0 || n < 0 || k % 32 != 0) return TQ4_E_SHAPE;
   if (m == 0 || n == 0) return TQ4_OK;
   if (y == nullptr) return TQ4_E_NULL;
-  if (!aligned(y, 4) || !aligned(tail.bias, 4) || !aligned(tail.residual, 4)) return TQ4_E_ALIGN;
+  const size_t elem = tail.bf16 ? 2 : 4;
+  if (!aligned(y, elem) || !aligned(tail.bias, 4) || !aligned(tail.residual, elem))
+    return TQ4_E_ALIGN;
   // the residual is read where y is written: the same array or disjoint
   if (tail.residual != nullptr && tail.residual != y) {
     const uintptr_t r0 = reinterpret_cast<uintptr_t>(tail.residual);
     const uintptr_t y0 = reinterpret_cast<uintptr_t>(y);
-    const uintptr_t bytes = static_cast<uintptr_t>(m) * static_cast<uintptr_t>(n) * sizeof(float);
+    const uintptr_t bytes = static_cast<uintptr_t>(m) * static_cast<uintptr_t>(n) * elem;
     if (r0 < y0 + bytes && y0 < r0 + bytes) return TQ4_E_SHAPE;
   }
   hipStream_t s = as_stream(stream);
-  const bool has_tail = tail.bias != nullptr || tail.residual != nullptr;
+  float *yf = static_cast<float *>(y);  // bf16 outputs are addressed as such by the kernels
+  const bool plain = tail.bias == nullptr && tail.residual == nullptr && !tail.bf16;
   if (k == 0)
-    return device_status(has_tail ? tq4::launch_tail_only(tail, m, n, y, s)
-                                  : tq4::launch_fill_zero(y, m * n, s));
+    return device_status(plain ? tq4::launch_fill_zero(yf, m * n, s)
+                               : tq4::launch_tail_only(tail, m, n, yf, s));
   if (x_bf16 == nullptr || packed == nullptr) return TQ4_E_NULL;
   if (!aligned(x_bf16, 16) || !aligned(packed, 4)) return TQ4_E_ALIGN;
   const LinearLayout l = linear_layout(m, k, n, false);
   const int ws_status = check_workspace(workspace, workspace_bytes, l.total);
   if (ws_status != TQ4_OK) return ws_status;
   if (tq4::skinny_fits(m, k, n))
-    return device_status(tq4::launch_skinny(x_bf16, m, k, packed, n, sign_bits, y, s, tail));
+    return device_status(tq4::launch_skinny(x_bf16, m, k, packed, n, sign_bits, yf, s, tail));
   char *ws = static_cast<char *>(workspace);
   uint16_t *xt = reinterpret_cast<uint16_t *>(ws + l.xt);
   hipError_t e = tq4::launch_act_rht_bf16(x_bf16, m, k, sign_bits, xt, s);
   if (e != hipSuccess) return TQ4_E_DEVICE;
   const DensePlan p = tq4::plan_dense(m, k, n);
-  e = tq4::launch_dense(p, xt, m, k, packed, n, y, reinterpret_cast<float *>(ws + l.partial), s,
+  e = tq4::launch_dense(p, xt, m, k, packed, n, yf, reinterpret_cast<float *>(ws + l.partial), s,
                         tail);
   return device_status(e);
 }
@@ -199,8 +202,16 @@ int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *pack
 int tq4_linear_epilogue(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed,
                         int64_t n, uint32_t sign_bits, const float *bias, const float *residual,
                         float *y, void *workspace, size_t workspace_bytes, void *stream) {
-  return linear_impl(x_bf16, m, k, packed, n, sign_bits, tq4::Tail{bias, residual}, y, workspace,
-                     workspace_bytes, stream);
+  return linear_impl(x_bf16, m, k, packed, n, sign_bits, tq4::Tail{bias, residual, 0}, y,
+                     workspace, workspace_bytes, stream);
+}
+
+int tq4_linear_epilogue_bf16(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed,
+                             int64_t n, uint32_t sign_bits, const float *bias,
+                             const uint16_t *residual_bf16, uint16_t *y_bf16, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  return linear_impl(x_bf16, m, k, packed, n, sign_bits, tq4::Tail{bias, residual_bf16, 1},
+                     y_bf16, workspace, workspace_bytes, stream);
 }
 
 int tq4_linear_rotated(const uint16_t *xt_f16, int64_t m, int64_t k, const uint8_t *packed,

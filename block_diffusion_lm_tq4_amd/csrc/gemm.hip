@@ -53,8 +53,7 @@ struct GemmArgs {
   float *out;                // output rows, stride n
   uint16_t *out16;           // MoE up: rotated hidden rows (fp16 bits), stride n
   float *partial;            // [ksplit][m][n] (dense split-K)
-  const float *bias;         // dense: [n] or null
-  const float *residual;     // dense: [m][n] or null (may equal out)
+  Tail tail;                 // dense: bias / residual / bf16 output
   const int32_t *perm;       // MoE: bucket position -> pair
   const MoETile *tiles;      // MoE tile list
   const int32_t *n_tiles;    // MoE tile count (device)
@@ -98,32 +97,35 @@ __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *l
 // compiler from moving a load above an earlier store; reordering by hand is
 // sound because each element is read and written by its own lane only.
 // kCheck = false: the whole grid lies inside the output (no bounds tests).
-template <bool kCheck, int MS, int NS>
-__device__ inline void store_tiles_impl(const floatx4 (&acc)[MS][NS], float *out,
-                                        const float *bias, const float *residual, int64_t m0,
-                                        int64_t n0, int64_t mlim, int64_t nlim, int grp, int r) {
-  float bv[NS];
+// kBF16: the residual and output are bf16 (the tail's flag, as a constant).
+template <bool kCheck, bool kBF16, int MS, int NS>
+__device__ inline void store_tiles_impl(const floatx4 (&acc)[MS][NS], float *out, const Tail &t,
+                                        int64_t m0, int64_t n0, int64_t mlim, int64_t nlim,
+                                        int grp, int r) {
+  // Loads use indices clamped into the output, so they need no branches;
+  // what they read for an element outside it is never stored.
+  const auto clamp_m = [&](int64_t m) { return kCheck && m >= mlim ? mlim - 1 : m; };
+  const auto clamp_n = [&](int64_t n) { return kCheck && n >= nlim ? nlim - 1 : n; };
+  float bv[NS];  // the bias of this lane's columns, loaded once
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int64_t n = n0 + 16 * j + r;
-    bv[j] = (bias != nullptr && (!kCheck || n < nlim)) ? bias[n] : 0.f;
-  }
+  for (int j = 0; j < NS; ++j) bv[j] = t.bias != nullptr ? t.bias[clamp_n(n0 + 16 * j + r)] : 0.f;
   constexpr int kIB = 2;  // row tiles per batch
 #pragma unroll
   for (int i0 = 0; i0 < MS; i0 += kIB) {
-    float yv[kIB][NS][4];
-    if (residual != nullptr) {
+    float y[kIB][NS][4];
+    if (t.residual != nullptr) {
 #pragma unroll
-      for (int ii = 0; ii < kIB; ++ii)
+      for (int ii = 0; ii < kIB; ++ii) {
+        if (i0 + ii >= MS) break;
 #pragma unroll
         for (int j = 0; j < NS; ++j)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int64_t m = m0 + 16 * (i0 + ii) + 4 * grp + v;
-            const int64_t n = n0 + 16 * j + r;
-            const bool in = i0 + ii < MS && (!kCheck || (m < mlim && n < nlim));
-            yv[ii][j][v] = in ? residual[m * nlim + n] : 0.f;
+            const int64_t m = clamp_m(m0 + 16 * (i0 + ii) + 4 * grp + v);
+            const int64_t n = clamp_n(n0 + 16 * j + r);
+            y[ii][j][v] = tail_residual_as<kBF16>(t.residual, m * nlim + n);
           }
+      }
     }
 #pragma unroll
     for (int ii = 0; ii < kIB; ++ii) {
@@ -132,10 +134,10 @@ __device__ inline void store_tiles_impl(const floatx4 (&acc)[MS][NS], float *out
       for (int j = 0; j < NS; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float y = acc[i0 + ii][j][v];
-          if (bias != nullptr) y += bv[j];
-          if (residual != nullptr) y += yv[ii][j][v];
-          yv[ii][j][v] = y;
+          float a = acc[i0 + ii][j][v];  // the same two adds, in order, as tail_sum
+          if (t.bias != nullptr) a += bv[j];
+          if (t.residual != nullptr) a += y[ii][j][v];
+          y[ii][j][v] = a;
         }
     }
 #pragma unroll
@@ -147,20 +149,29 @@ __device__ inline void store_tiles_impl(const floatx4 (&acc)[MS][NS], float *out
         for (int v = 0; v < 4; ++v) {
           const int64_t m = m0 + 16 * (i0 + ii) + 4 * grp + v;
           const int64_t n = n0 + 16 * j + r;
-          if (!kCheck || (m < mlim && n < nlim)) out[m * nlim + n] = yv[ii][j][v];
+          if (!kCheck || (m < mlim && n < nlim))
+            tail_store_as<kBF16>(out, m * nlim + n, y[ii][j][v]);
         }
     }
   }
 }
 
 template <int MS, int NS>
-__device__ inline void store_tiles(const floatx4 (&acc)[MS][NS], float *out, const float *bias,
-                                   const float *residual, int64_t m0, int64_t n0, int64_t mlim,
-                                   int64_t nlim, int grp, int r) {
-  if (m0 + 16 * MS <= mlim && n0 + 16 * NS <= nlim)
-    store_tiles_impl<false>(acc, out, bias, residual, m0, n0, mlim, nlim, grp, r);
-  else
-    store_tiles_impl<true>(acc, out, bias, residual, m0, n0, mlim, nlim, grp, r);
+__device__ inline void store_tiles(const floatx4 (&acc)[MS][NS], float *out, const Tail &t,
+                                   int64_t m0, int64_t n0, int64_t mlim, int64_t nlim, int grp,
+                                   int r) {
+  const bool full = m0 + 16 * MS <= mlim && n0 + 16 * NS <= nlim;
+  if (t.bf16) {
+    if (full)
+      store_tiles_impl<false, true>(acc, out, t, m0, n0, mlim, nlim, grp, r);
+    else
+      store_tiles_impl<true, true>(acc, out, t, m0, n0, mlim, nlim, grp, r);
+  } else {
+    if (full)
+      store_tiles_impl<false, false>(acc, out, t, m0, n0, mlim, nlim, grp, r);
+    else
+      store_tiles_impl<true, false>(acc, out, t, m0, n0, mlim, nlim, grp, r);
+  }
 }
 
 __device__ inline half2v scale_pair(uint32_t bf16_bits) {
@@ -363,8 +374,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
     // split-K partial sums take the tail in the reduction
     const bool split_k = g.ksplit > 1;
     float *dst = split_k ? g.partial + static_cast<int64_t>(split) * g.m * g.n : g.out;
-    store_tiles(acc, dst, split_k ? nullptr : g.bias, split_k ? nullptr : g.residual, m_base,
-                n_base + wave * (16 * NSUB), g.m, g.n, grp, r);
+    store_tiles(acc, dst, split_k ? Tail{} : g.tail, m_base, n_base + wave * (16 * NSUB), g.m,
+                g.n, grp, r);
   } else if constexpr (MODE == kMoEUp) {
     // h = relu(u)^2, then its rotation ht = H32 diag(s) h / sqrt(32), stored
     // as fp16: a wave's 32 output columns are one 32-block of h (NSUB == 2).
@@ -673,8 +684,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_big_kernel(GemmArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding chunks' loads
 
-  store_tiles(acc, g.out, g.bias, g.residual, m_base, n_base + wave * (16 * kBigNSub), g.m, g.n,
-              grp, r);
+  store_tiles(acc, g.out, g.tail, m_base, n_base + wave * (16 * kBigNSub), g.m, g.n, grp, r);
 }
 
 // Dense large-M variant with two waves on every SIMD.  Tile: 256 activation
@@ -860,8 +870,8 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding chunks' loads
 
-  store_tiles(acc, g.out, g.bias, g.residual, m_base + wm * (16 * kHugeMSub),
-              n_base + wn * (16 * kHugeNSub), g.m, g.n, grp, r);
+  store_tiles(acc, g.out, g.tail, m_base + wm * (16 * kHugeMSub), n_base + wn * (16 * kHugeNSub),
+              g.m, g.n, grp, r);
 }
 
 // y[i] = sum over splits of partial[s][i], in split order, then the tail.
@@ -873,7 +883,9 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__res
   if (i >= mn) return;
   float s = partial[i];
   for (int q = 1; q < ksplit; ++q) s += partial[q * mn + i];
-  y[i] = add_tail(s, tail.bias, tail.residual, i / n, i % n, n);
+  const int64_t col = tail.bias != nullptr ? i % n : 0;  // the column only feeds the bias
+  const float res = tail.residual != nullptr ? tail_residual(tail, i) : 0.f;
+  tail_store(tail, y, i, tail_sum(tail, s, col, res));
 }
 
 template <int MSUB, int NSUB, int LUTC, int MODE>
@@ -956,8 +968,7 @@ hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64
   g.w = packed;
   g.out = y;
   g.partial = partial;
-  g.bias = tail.bias;
-  g.residual = tail.residual;
+  g.tail = tail;
   g.m = m;
   g.n = n;
   g.k = k;

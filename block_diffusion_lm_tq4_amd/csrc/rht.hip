@@ -38,7 +38,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
 // y = bias + residual, for a product with an empty k.
 __global__ __launch_bounds__(256) void tail_only_kernel(Tail t, int64_t m, int64_t n, float *y) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < m * n) y[i] = add_tail(0.f, t.bias, t.residual, i / n, i % n, n);
+  if (i >= m * n) return;
+  const int64_t col = t.bias != nullptr ? i % n : 0;  // the column only feeds the bias
+  const float res = t.residual != nullptr ? tail_residual(t, i) : 0.f;
+  tail_store(t, y, i, tail_sum(t, 0.f, col, res));
 }
 
 }  // namespace

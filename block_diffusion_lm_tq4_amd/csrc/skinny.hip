@@ -63,8 +63,7 @@ struct SkinnyArgs {
   const uint16_t *x;  // bf16 [m][k]
   const uint8_t *w;   // packed [n][k/32][20]
   float *y;           // [m][n]
-  const float *bias;      // [n] or null
-  const float *residual;  // [m][n] or null (may equal y)
+  Tail tail;          // bias / residual / bf16 output
   int32_t m, n, kb;   // kb = k / 32
   uint32_t sign_bits;
   Codebook cb;
@@ -274,9 +273,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * grp + v;
-        if (m < g.m)
-          g.y[static_cast<int64_t>(m) * g.n + n] =
-              add_tail(s[v] * rs32, g.bias, g.residual, m, n, g.n);
+        if (m < g.m) tail_apply(g.tail, g.y, m, n, g.n, s[v] * rs32);
       }
     }
   }
@@ -500,9 +497,7 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
     for (int w = 1; w < kDmaConsumers; ++w) sum += red[((w * kRowTiles + j) * 4 + v) * 64 + lane];
     const int n = n0 + r + 16 * j;
     const int m = 4 * grp + v;
-    if (n < g.n && m < g.m)
-      g.y[static_cast<int64_t>(m) * g.n + n] =
-          add_tail(sum * 0x1.6a09e6p-3f, g.bias, g.residual, m, n, g.n);
+    if (n < g.n && m < g.m) tail_apply(g.tail, g.y, m, n, g.n, sum * 0x1.6a09e6p-3f);
   }
 }
 
@@ -543,8 +538,7 @@ hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t 
   a.x = x;
   a.w = packed;
   a.y = y;
-  a.bias = tail.bias;
-  a.residual = tail.residual;
+  a.tail = tail;
   a.m = static_cast<int32_t>(m);
   a.n = static_cast<int32_t>(n);
   a.kb = static_cast<int32_t>(k / 32);

@@ -62,23 +62,63 @@ __device__ inline void rotate_block_bf16(const uint16_t *x, uint32_t sign_bits, 
   }
 }
 
-// The linear layer's additive tail on one output element: acc + bias[n] +
-// residual[m, n] (either pointer may be null), in that order, fp32.  No
-// contraction: the first add is never fused with the product's last multiply,
-// so the result is the rounded product plus the tail, as two separate adds.
-__device__ inline float add_tail(float acc, const float *bias, const float *residual, int64_t m,
-                                 int64_t n, int64_t ldn) {
+// The linear layer's additive tail: y[m, n] = acc + bias[n] + residual[m, n],
+// either term optional, summed in fp32 in that order.  With bf16 set, the
+// residual and the output are bf16 and the fp32 sum is rounded once, to
+// nearest even.  The residual may be the output itself: every element is read
+// and then written by one thread.
+struct Tail {
+  const float *bias;     // [n] fp32, or null
+  const void *residual;  // [m, n], or null
+  int32_t bf16;          // 0: residual and output fp32; 1: both bf16
+};
+
+template <bool kBF16>
+__device__ inline float tail_residual_as(const void *residual, int64_t i) {
+  if constexpr (kBF16)
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(residual)[i]) << 16);
+  else
+    return static_cast<const float *>(residual)[i];
+}
+
+template <bool kBF16>
+__device__ inline void tail_store_as(float *out, int64_t i, float v) {
+  if constexpr (kBF16)
+    reinterpret_cast<uint16_t *>(out)[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+  else
+    out[i] = v;
+}
+
+__device__ inline float tail_residual(const Tail &t, int64_t i) {
+  return t.bf16 ? tail_residual_as<true>(t.residual, i) : tail_residual_as<false>(t.residual, i);
+}
+
+// acc plus the tail's terms for column n, given the residual value (ignored
+// without a residual).  No contraction: the first add is never fused with the
+// product's last multiply, so the result is the rounded product plus the
+// tail, as separate adds.
+__device__ inline float tail_sum(const Tail &t, float acc, int64_t n, float res) {
 #pragma clang fp contract(off)
-  if (bias != nullptr) acc += bias[n];
-  if (residual != nullptr) acc += residual[m * ldn + n];
+  if (t.bias != nullptr) acc += t.bias[n];
+  if (t.residual != nullptr) acc += res;
   return acc;
 }
 
-// Bias and residual of a dense product (both may be null).
-struct Tail {
-  const float *bias;      // [n]
-  const float *residual;  // [m, n], may equal y
-};
+// Stores one output element (fp32, or bf16 rounded to nearest even).
+__device__ inline void tail_store(const Tail &t, float *out, int64_t i, float v) {
+  if (t.bf16)
+    tail_store_as<true>(out, i, v);
+  else
+    tail_store_as<false>(out, i, v);
+}
+
+// The whole tail of element (m, n) of an output with row stride ldn.
+__device__ inline void tail_apply(const Tail &t, float *out, int64_t m, int64_t n, int64_t ldn,
+                                  float acc) {
+  const int64_t i = m * ldn + n;
+  const float res = t.residual != nullptr ? tail_residual(t, i) : 0.f;
+  tail_store(t, out, i, tail_sum(t, acc, n, res));
+}
 
 // ---- launchers (return hipSuccess or the launch error) --------------------
 hipError_t launch_pack(const float *w, int64_t n_blocks, uint32_t sign_bits,

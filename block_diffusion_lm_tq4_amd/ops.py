@@ -120,14 +120,7 @@ def linear(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
     return out
 
 
-def linear_epilogue(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
-                    bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
-                    out: torch.Tensor | None = None,
-                    workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """y = x . W_hat^T + bias + residual, fp32 [m, n] (tq4_linear_epilogue).
-
-    bias is fp32 [n] or None; residual is fp32 [m, n] or None and may be `out`
-    itself (the sum is then taken in place)."""
+def _linear_tail(fn: str, x, packed, sign_bits, bias, residual, out, workspace, ydtype):
     _cuda_contig(x, "x", torch.bfloat16)
     _cuda_contig(packed, "packed", torch.uint8)
     _require(x.dim() == 2, "x must be [m, k]")
@@ -139,21 +132,43 @@ def linear_epilogue(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
         _cuda_contig(bias, "bias", torch.float32)
         _require(tuple(bias.shape) == (n,), "bias must be [n]")
     if residual is not None:
-        _cuda_contig(residual, "residual", torch.float32)
+        _cuda_contig(residual, "residual", ydtype)
         _require(tuple(residual.shape) == (m, n), "residual must be [m, n]")
     if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _cuda_contig(out, "out", torch.float32)
+        out = torch.empty((m, n), dtype=ydtype, device=x.device)
+    _cuda_contig(out, "out", ydtype)
     _require(tuple(out.shape) == (m, n), "out must be [m, n]")
     need = linear_workspace_size(m, k, n)
     if workspace is None:
         workspace = _WS.get(x.device, "linear", need)
-    check("tq4_linear_epilogue",
-          lib().tq4_linear_epilogue(x.data_ptr(), m, k, packed.data_ptr(), n,
-                                    sign_bits & 0xFFFFFFFF, _ptr(bias), _ptr(residual),
-                                    out.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                                    _stream(x.device)))
+    check(fn, getattr(lib(), fn)(x.data_ptr(), m, k, packed.data_ptr(), n, sign_bits & 0xFFFFFFFF,
+                                 _ptr(bias), _ptr(residual), out.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel(), _stream(x.device)))
     return out
+
+
+def linear_epilogue(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
+                    bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x . W_hat^T + bias + residual, fp32 [m, n] (tq4_linear_epilogue).
+
+    bias is fp32 [n] or None; residual is fp32 [m, n] or None and may be `out`
+    itself (the sum is then taken in place)."""
+    return _linear_tail("tq4_linear_epilogue", x, packed, sign_bits, bias, residual, out,
+                        workspace, torch.float32)
+
+
+def linear_epilogue_bf16(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
+                         bias: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+                         out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16(x . W_hat^T + bias + residual), bf16 [m, n] (tq4_linear_epilogue_bf16).
+
+    bias is fp32 [n] or None; residual is bf16 [m, n] or None and may be `out`
+    itself.  The sum is formed in fp32 and rounded once."""
+    return _linear_tail("tq4_linear_epilogue_bf16", x, packed, sign_bits, bias, residual, out,
+                        workspace, torch.bfloat16)
 
 
 def linear_rotated(xt: torch.Tensor, packed: torch.Tensor, out: torch.Tensor | None = None,

@@ -153,6 +153,25 @@ int tq4_linear_epilogue(const uint16_t *x_bf16, int64_t m, int64_t k,
                         const float *bias, const float *residual, float *y,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* tq4_linear_epilogue with a bf16 residual stream and bf16 output, the form
+ * the next layer reads (the model runs in BF16; model card, Reproduction):
+ * y_bf16[m, n] = bf16(product + bias[n] + residual[m, n]), the sum taken in
+ * fp32 as in tq4_linear_epilogue and rounded once, to nearest even.  The
+ * result is the bf16 rounding of tq4_linear_epilogue's fp32 result on the
+ * same inputs (residual widened exactly), bit for bit.
+ *   bias          : [n] fp32, device, 4-byte aligned, or NULL
+ *   residual_bf16 : [m, n] bf16 bit patterns, device, 2-byte aligned, or
+ *                   NULL; may be y_bf16 itself, must not otherwise overlap it
+ *   y_bf16        : [m, n] bf16 bit patterns, device, 2-byte aligned
+ * The rounding adds at most 2^-9 of |y| per element to the fp32 result's
+ * error.  Workspace, errors and determinism as tq4_linear_epilogue; k == 0
+ * writes bf16(bias + residual). */
+int tq4_linear_epilogue_bf16(const uint16_t *x_bf16, int64_t m, int64_t k,
+                             const uint8_t *packed, int64_t n, uint32_t sign_bits,
+                             const float *bias, const uint16_t *residual_bf16,
+                             uint16_t *y_bf16, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
 /* Stable bucketing of the t*topk (token, slot) pairs by expert, the routing
  * step of the sync-free MoE (model card, Running it; 128 experts, top-6 in
  * The model underneath).  Pair p = token * topk + slot.

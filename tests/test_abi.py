@@ -142,6 +142,30 @@ def test_linear_epilogue_argument_errors(L):
     assert call(m=0) == OK and call(n=0) == OK
 
 
+def test_linear_epilogue_bf16_argument_errors(L):
+    ws = L.tq4_linear_workspace_size(100, 2688, 8192)
+    y = FAKE
+    args = dict(x=FAKE, m=100, k=2688, p=FAKE, n=8192, sb=0, b=FAKE, r=FAKE + (1 << 24), y=y,
+                ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.tq4_linear_epilogue_bf16(a["x"], a["m"], a["k"], a["p"], a["n"], a["sb"],
+                                          a["b"], a["r"], a["y"], a["ws"], a["wsb"], None)
+
+    assert call(y=None) == E_NULL
+    assert call(y=FAKE + 1) == E_ALIGN
+    assert call(r=FAKE + (1 << 24) + 1) == E_ALIGN
+    assert call(b=FAKE + 2) == E_ALIGN
+    # bf16 arrays are 2-byte aligned and span 100 * 8192 * 2 bytes
+    assert call(y=FAKE + 2, r=FAKE + 2 + 100 * 8192 * 2, ws=None) == E_WS
+    assert call(r=y + 2) == E_SHAPE
+    assert call(r=y + 100 * 8192 * 2 - 2) == E_SHAPE
+    assert call(r=y + 100 * 8192 * 2, ws=None) == E_WS
+    assert call(r=y, ws=None) == E_WS
+    assert call(m=0) == OK
+
+
 def test_moe_argument_errors(L):
     ws = L.tq4_moe_workspace_size(16, 6, 128, 1856, 2688)
     assert ws > 0
