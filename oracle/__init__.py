@@ -6,5 +6,9 @@ product path (the HIP library and its Python binding) never imports, calls or
 links it, and it shares no code, table or constant generator with that path.
 """
 
+from .fp8_oracle import *  # noqa: F401,F403
+from .fp8_oracle import __all__ as _fp8_all
 from .tq4_oracle import *  # noqa: F401,F403
-from .tq4_oracle import __all__  # noqa: F401
+from .tq4_oracle import __all__ as _tq4_all
+
+__all__ = list(_tq4_all) + list(_fp8_all)
