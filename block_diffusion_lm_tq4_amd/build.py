@@ -32,6 +32,7 @@ SOURCES = {
     "skinny.hip": [],
     "moe.hip": [],
     "probe.hip": [],
+    "fp8.hip": ["-ffp-contract=off"],
 }
 
 ARCH = "gfx950"

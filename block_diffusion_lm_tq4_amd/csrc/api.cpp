@@ -299,6 +299,77 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t 
   return device_status(e);
 }
 
+// ---- fp8 weight cache ---------------------------------------------------
+
+namespace {
+
+bool fp8_sizes_ok(int64_t rows, int64_t k) {
+  return rows >= 0 && k >= 0 && k % 32 == 0 && (k == 0 || tq4::fp8_shape_fits(1, k, 1));
+}
+
+size_t fp8_rows_bytes(int64_t rows, int64_t k) {
+  const int64_t kp = tq4::fp8_padded_k(k);
+  return static_cast<size_t>(rows) * static_cast<size_t>(kp) +
+         static_cast<size_t>(rows) * static_cast<size_t>(kp / 32);
+}
+
+}  // namespace
+
+size_t tq4_fp8_cache_size(int64_t n, int64_t k) {
+  if (!fp8_sizes_ok(n, k) || k == 0) return 0;
+  return fp8_rows_bytes(n, k);
+}
+
+int tq4_fp8_cache(const uint8_t *packed, int64_t n, int64_t k, uint32_t sign_bits, uint8_t *cache,
+                  void *stream) {
+  if (!fp8_sizes_ok(n, k)) return TQ4_E_SHAPE;
+  if (n == 0 || k == 0) return TQ4_OK;
+  if (packed == nullptr || cache == nullptr) return TQ4_E_NULL;
+  if (!aligned(packed, 4) || !aligned(cache, 16)) return TQ4_E_ALIGN;
+  const int64_t kp = tq4::fp8_padded_k(k);
+  return device_status(tq4::launch_fp8_cache(packed, n, k, sign_bits, cache, cache + n * kp,
+                                             as_stream(stream)));
+}
+
+int tq4_act_mxfp8(const uint16_t *x_bf16, int64_t m, int64_t k, uint8_t *codes, uint8_t *scales,
+                  void *stream) {
+  if (!fp8_sizes_ok(m, k)) return TQ4_E_SHAPE;
+  if (m == 0 || k == 0) return TQ4_OK;
+  if (x_bf16 == nullptr || codes == nullptr || scales == nullptr) return TQ4_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(codes, 16)) return TQ4_E_ALIGN;
+  return device_status(tq4::launch_act_mxfp8(x_bf16, m, k, codes, scales, as_stream(stream)));
+}
+
+size_t tq4_linear_fp8_workspace_size(int64_t m, int64_t k, int64_t n) {
+  if (!fp8_sizes_ok(m, k) || n < 0) return 0;
+  if (m == 0 || n == 0 || k == 0) return 0;
+  const int64_t kp = tq4::fp8_padded_k(k);
+  return align_up(static_cast<size_t>(m) * static_cast<size_t>(kp)) +
+         align_up(static_cast<size_t>(m) * static_cast<size_t>(kp / 32));
+}
+
+int tq4_linear_fp8(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *cache, int64_t n,
+                   float *y, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!fp8_sizes_ok(m, k) || n < 0) return TQ4_E_SHAPE;
+  if (m == 0 || n == 0) return TQ4_OK;
+  if (y == nullptr) return TQ4_E_NULL;
+  if (!aligned(y, 4)) return TQ4_E_ALIGN;
+  hipStream_t s = as_stream(stream);
+  if (k == 0) return device_status(tq4::launch_fill_zero(y, m * n, s));
+  if (x_bf16 == nullptr || cache == nullptr) return TQ4_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(cache, 16)) return TQ4_E_ALIGN;
+  const int ws_status =
+      check_workspace(workspace, workspace_bytes, tq4_linear_fp8_workspace_size(m, k, n));
+  if (ws_status != TQ4_OK) return ws_status;
+  const int64_t kp = tq4::fp8_padded_k(k);
+  uint8_t *xq = static_cast<uint8_t *>(workspace);
+  uint8_t *xs = xq + align_up(static_cast<size_t>(m) * static_cast<size_t>(kp));
+  hipError_t e = tq4::launch_act_mxfp8(x_bf16, m, k, xq, xs, s);
+  if (e != hipSuccess) return TQ4_E_DEVICE;
+  return device_status(
+      tq4::launch_linear_fp8(xq, xs, m, k, cache, cache + n * kp, n, y, s));
+}
+
 int tq4_read_probe(const void *src, int64_t bytes, float *sink, void *stream) {
   if (bytes < 0 || bytes % 16 != 0) return TQ4_E_SHAPE;
   if (bytes == 0) return TQ4_OK;

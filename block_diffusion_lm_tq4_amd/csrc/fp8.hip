@@ -1,0 +1,545 @@
+// fp8 weight-cache variant of the linear layer (Nemotron-TheHobbit-30B-A3B
+// model card, Help wanted: decode the weights once into a resident fp8 copy,
+// about 63 GB for both towers, so that no forward pass decodes).
+//
+// Storage (MXFP8): OCP e4m3 codes, one power-of-two scale 2^e per 32
+// consecutive k of a row, kept as the E8M0 byte e + 127; e is the smallest
+// integer in [-127, 127] with the block's largest magnitude <= 448 * 2^e.
+// Rows are padded to kp = k rounded up to a multiple of 128 (zero codes, zero
+// scale bytes), so every 128-k step is whole and every row of scales is
+// 4-byte aligned.  The cache holds the decoded weights W_hat (rotation undone); activations
+// are quantized the same way per call, and the product runs on the
+// block-scaled fp8 MFMA of gfx950 (v_mfma_scale_f32_16x16x128_f8f6f4), whose
+// per-32 scales are exactly these blocks.
+//
+// Operand layout of that instruction with 8-bit data (measured on the
+// device): lane l = i + 16 g holds 32 bytes of row i: bytes 0-15 are
+// k = 16 g .. 16 g + 15 and bytes 16-31 are k = 64 + 16 g .. 64 + 16 g + 15
+// of the 128-k step; the B operand is laid out the same way per column.  The
+// scale operand of lane i + 16 b (its low byte) scales k = 32 b .. 32 b + 31
+// of row i.  The accumulator layout is that of the 16x16 f16 MFMAs.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq4_internal.h"
+
+namespace tq4 {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---------------------------------------------------------------------------
+// Encoding
+
+// Nearest e4m3 code to v (|v| <= 448), ties to the even code, from fp64 with
+// one rounding: |v| = mant * 2^E with mant in [1, 2) gives the 3-bit mantissa
+// rint((mant - 1) * 8), exact in fp64; below 2^-6 the grid is 2^-9 apart.
+__device__ inline uint32_t e4m3_from_f64(double v) {
+  const uint32_t sign = __builtin_signbit(v) ? 0x80u : 0u;
+  const double a = __builtin_fabs(v);
+  if (a < 0x1p-6) return sign | static_cast<uint32_t>(__builtin_rint(a * 512.0));  // 8 = 2^-6
+  int p;
+  const double f = __builtin_frexp(a, &p);  // a = f * 2^p, f in [0.5, 1)
+  int e = p - 1;
+  double r = __builtin_rint((2.0 * f - 1.0) * 8.0);
+  if (r == 8.0) {
+    r = 0.0;
+    ++e;
+  }
+  return sign | (static_cast<uint32_t>(e + 7) << 3) | static_cast<uint32_t>(r);
+}
+
+// The block exponent for a largest magnitude amax: 448 = 0.875 * 2^9, so with
+// amax = f * 2^p (f in [0.5, 1)) it is p - 9, plus one when f > 0.875.
+__device__ inline int block_exponent(double amax) {
+  if (amax == 0.0) return -127;
+  int p;
+  const double f = __builtin_frexp(amax, &p);
+  int e = p - 9 + (f > 0.875 ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+__device__ inline int block_exponent_f32(float amax) {
+  if (amax == 0.f) return -127;
+  int p;
+  const float f = __builtin_frexpf(amax, &p);
+  int e = p - 9 + (f > 0.875f ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// One thread per 32-weight block: z_hat = S_h * c_q, w_hat = s * H32 z_hat
+// * (1/sqrt 32) in fp64 (the butterfly's sums are exact while the two
+// half-block scales are within 2^12 of each other), then the block exponent
+// and the e4m3 codes of w_hat / 2^e.
+// Thread t covers block t % kpb of row t / kpb (kpb = kp / 32 blocks per
+// padded row); padding blocks are written as zeros.
+__global__ __launch_bounds__(256) void fp8_cache_kernel(const uint8_t *__restrict__ packed,
+                                                        int64_t n, int32_t kb, int32_t kpb,
+                                                        uint32_t sign_bits, Codebook cb,
+                                                        uint8_t *__restrict__ codes,
+                                                        uint8_t *__restrict__ scales) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= n * kpb) return;
+  const int64_t row = t / kpb;
+  const int32_t col = static_cast<int32_t>(t % kpb);
+  uint4 *dst = reinterpret_cast<uint4 *>(codes + t * 32);
+  if (col >= kb) {
+    dst[0] = make_uint4(0u, 0u, 0u, 0u);
+    dst[1] = make_uint4(0u, 0u, 0u, 0u);
+    scales[t] = 0;
+    return;
+  }
+  const uint32_t *p = reinterpret_cast<const uint32_t *>(packed + (row * kb + col) * 20);
+  uint32_t wd[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) wd[i] = p[i];
+  const double s0 = static_cast<double>(__uint_as_float((wd[4] & 0xFFFFu) << 16));
+  const double s1 = static_cast<double>(__uint_as_float(wd[4] & 0xFFFF0000u));
+  double v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t byte = (wd[i / 8] >> (8 * ((i / 2) % 4))) & 0xFFu;
+    const uint32_t q = (i % 2 == 0) ? (byte & 15u) : (byte >> 4);
+    v[i] = (i < 16 ? s0 : s1) * static_cast<double>(cb.c[q]);
+  }
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const double a = v[i], c = v[i + h];
+        v[i] = a + c;
+        v[i + h] = a - c;
+      }
+    }
+  }
+  const double rs32 = 0x1.6a09e667f3bcdp-3;  // 1/sqrt(32) rounded to fp64
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] *= rs32;
+    if ((sign_bits >> i) & 1u) v[i] = -v[i];
+    amax = __builtin_fmax(amax, __builtin_fabs(v[i]));
+  }
+  const int e = block_exponent(amax);
+  uint32_t out[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      word |= e4m3_from_f64(__builtin_ldexp(v[4 * w + t], -e)) << (8 * t);
+    out[w] = word;
+  }
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  scales[t] = static_cast<uint8_t>(e + 127);
+}
+
+// One thread per 32-element activation block: bf16 -> fp32 (exact), block
+// exponent, codes of x / 2^e (exact scaling, then one hardware rounding to
+// nearest even).
+__global__ __launch_bounds__(256) void act_mxfp8_kernel(const uint16_t *__restrict__ x,
+                                                        int64_t m, int32_t kb, int32_t kpb,
+                                                        uint8_t *__restrict__ codes,
+                                                        uint8_t *__restrict__ scales) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= m * kpb) return;
+  const int64_t row = t / kpb;
+  const int32_t col = static_cast<int32_t>(t % kpb);
+  uint4 *dst = reinterpret_cast<uint4 *>(codes + t * 32);
+  if (col >= kb) {
+    dst[0] = make_uint4(0u, 0u, 0u, 0u);
+    dst[1] = make_uint4(0u, 0u, 0u, 0u);
+    scales[t] = 0;
+    return;
+  }
+  const uint4 *src = reinterpret_cast<const uint4 *>(x + (row * kb + col) * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 d = src[i];
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  const int e = block_exponent_f32(amax);
+  uint32_t out[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(v[4 * w], -e),
+                                              __builtin_ldexpf(v[4 * w + 1], -e), 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(v[4 * w + 2], -e),
+                                          __builtin_ldexpf(v[4 * w + 3], -e), word, true);
+    out[w] = static_cast<uint32_t>(word);
+  }
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  scales[t] = static_cast<uint8_t>(e + 127);
+}
+
+// ---------------------------------------------------------------------------
+// Products
+
+struct F8Args {
+  const uint8_t *xq;  // activation codes [m][kp]
+  const uint8_t *xs;  // activation scales [m][kp/32]
+  const uint8_t *wq;  // weight codes [n][kp]
+  const uint8_t *ws;  // weight scales [n][kp/32]
+  float *y;           // [m][n]
+  int64_t m, n;
+  int64_t kp;         // padded k, a multiple of 128
+  int32_t kpb;        // kp / 32
+  int32_t chunks;     // kp / 128
+  int32_t tiles_m, tiles_n;
+};
+
+__device__ inline intx8 join(uint4 lo, uint4 hi) {
+  intx8 r;
+  r[0] = static_cast<int>(lo.x); r[1] = static_cast<int>(lo.y);
+  r[2] = static_cast<int>(lo.z); r[3] = static_cast<int>(lo.w);
+  r[4] = static_cast<int>(hi.x); r[5] = static_cast<int>(hi.y);
+  r[6] = static_cast<int>(hi.z); r[7] = static_cast<int>(hi.w);
+  return r;
+}
+
+// Small M (<= 16 * MT): one workgroup of four waves per 16 output columns;
+// wave w takes the 128-k steps w, w + 4, ...; within a batch of CB steps every
+// load is issued before the first product.  Partial sums meet in LDS and are
+// added in wave order.
+constexpr int kF8SkWaves = 4;
+
+template <int MT>
+constexpr int f8_batch() {
+  return MT == 1 ? 6 : (MT == 2 ? 4 : 2);
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * kF8SkWaves) void fp8_skinny_kernel(F8Args g) {
+  constexpr int CB = f8_batch<MT>();
+  __shared__ floatx4 red[kF8SkWaves][MT][64];
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int r = lane % 16;
+  const int grp = lane / 16;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t nl = n0 + r < g.n ? n0 + r : g.n - 1;  // rows past n read row n - 1
+  const uint8_t *wrow = g.wq + nl * g.kp + 16 * grp;
+  const uint8_t *wsrow = g.ws + nl * g.kpb + grp;
+  const uint8_t *xrow[MT];
+  const uint8_t *xsrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t ml = 16 * t + r < g.m ? 16 * t + r : g.m - 1;
+    xrow[t] = g.xq + ml * g.kp + 16 * grp;
+    xsrow[t] = g.xs + ml * g.kpb + grp;
+  }
+  floatx4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = wave; c0 < g.chunks; c0 += CB * kF8SkWaves) {
+    uint4 b[CB][2];
+    uint4 a[CB][MT][2];
+    int sb[CB];
+    int sa[CB][MT];
+#pragma unroll
+    for (int s = 0; s < CB; ++s) {
+      // A step past the end reloads the last one with both scale bytes 0
+      // (2^-127 each): its products, at most 448^2 * 128 * 2^-254, round to
+      // zero in fp32, so it adds exactly nothing.  Every load and product
+      // stays unconditional, so all loads of the batch are in flight at once.
+      const int c_raw = c0 + s * kF8SkWaves;
+      const bool live = c_raw < g.chunks;
+      const int c = live ? c_raw : g.chunks - 1;
+      const int64_t k0 = 128 * static_cast<int64_t>(c);
+      b[s][0] = *reinterpret_cast<const uint4 *>(wrow + k0);
+      b[s][1] = *reinterpret_cast<const uint4 *>(wrow + k0 + 64);
+      const int wsc = wsrow[4 * c];
+      sb[s] = live ? wsc : 0;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        a[s][t][0] = *reinterpret_cast<const uint4 *>(xrow[t] + k0);
+        a[s][t][1] = *reinterpret_cast<const uint4 *>(xrow[t] + k0 + 64);
+        const int xsc = xsrow[t][4 * c];
+        sa[s][t] = live ? xsc : 0;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < CB; ++s) {
+      const intx8 bv = join(b[s][0], b[s][1]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            join(a[s][t][0], a[s][t][1]), bv, acc[t], 0, 0, 0, sa[s][t], 0, sb[s]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  if (wave < MT) {
+    floatx4 s = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < kF8SkWaves; ++w) s += red[w][wave][lane];
+    const int64_t n = n0 + r;
+    if (n < g.n) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = 16 * wave + 4 * grp + v;
+        if (m < g.m) g.y[m * g.n + n] = s[v];
+      }
+    }
+  }
+}
+
+// Large M: 256 x 128 output tile per workgroup of 8 waves (4 along m, 2
+// along n; each 64 x 64 as 4 x 4 tiles of 16 x 16), two waves per SIMD.  Per
+// 128-k step the tile's activation rows (256 x 128 bytes), weight rows
+// (128 x 128 bytes) and their scale words (4 bytes per row) go to LDS by
+// LDS-direct buffer loads into three stages, two steps ahead.  Piece p of an
+// operand's stage (1 KB) holds rows 8p .. 8p + 7: lane l fills row 8p + l / 8
+// at 16-byte slot l % 8 with global piece slot ^ ((row / 2) % 8), so the 16
+// rows of a fragment read hit distinct bank groups.
+constexpr int kF8Waves = 8;
+constexpr int kF8MSub = 4;
+constexpr int kF8NSub = 4;
+constexpr int kF8TM = 256;
+constexpr int kF8TN = 128;
+constexpr int kF8Row = 128;
+constexpr int kF8ALoads = kF8TM * kF8Row / 1024 / kF8Waves;  // 4
+constexpr int kF8WLoads = kF8TN * kF8Row / 1024 / kF8Waves;  // 2
+constexpr int kF8Loads = kF8ALoads + kF8WLoads + 1;           // + one scale load
+constexpr int kF8Stage = (kF8TM + kF8TN) * kF8Row + 512 * 4;  // data, then 512 scale words
+constexpr int kF8BufferFlags = 0x00020000;
+
+__global__ __launch_bounds__(64 * kF8Waves) void fp8_gemm_kernel(F8Args g) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[kF8Stage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[kF8Stage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage2[kF8Stage];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int r = lane % 16;
+  const int grp = lane / 16;
+  const int wm = wave / 2;
+  const int wn = wave % 2;
+
+  // XCD-banded tile order: consecutive workgroups go to different XCDs, so
+  // each XCD keeps one band of activation rows in its L2
+  int mt, nt;
+  {
+    const int id = static_cast<int>(blockIdx.x);
+    if (g.tiles_m % 8 == 0) {
+      const int band = g.tiles_m / 8;
+      const int j = id / 8;
+      mt = (id % 8) * band + j % band;
+      nt = j / band;
+    } else {
+      mt = id / g.tiles_n;
+      nt = id % g.tiles_n;
+    }
+  }
+  const int64_t m_base = static_cast<int64_t>(mt) * kF8TM;
+  const int64_t n_base = static_cast<int64_t>(nt) * kF8TN;
+  const int64_t rows_valid = g.m - m_base;
+  const int64_t cols_valid = g.n - n_base;
+  const int kp = static_cast<int>(g.kp);
+  const int kpb = g.kpb;
+
+  // data: rows past the matrix read row 0 (their results are not stored)
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.xq + m_base * g.kp), static_cast<short>(0), kF8TM * kp,
+      kF8BufferFlags);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.wq + n_base * g.kp), static_cast<short>(0), kF8TN * kp,
+      kF8BufferFlags);
+  uint32_t aoff[kF8ALoads], woff[kF8WLoads];
+#pragma unroll
+  for (int i = 0; i < kF8ALoads; ++i) {
+    const int row = 8 * (kF8ALoads * wave + i) + lane / 8;
+    const int piece = (lane % 8) ^ ((row >> 1) % 8);
+    aoff[i] = static_cast<uint32_t>((row < rows_valid ? row : 0) * kp + 16 * piece);
+  }
+#pragma unroll
+  for (int i = 0; i < kF8WLoads; ++i) {
+    const int row = 8 * (kF8WLoads * wave + i) + lane / 8;
+    const int piece = (lane % 8) ^ ((row >> 1) % 8);
+    woff[i] = static_cast<uint32_t>((row < cols_valid ? row : 0) * kp + 16 * piece);
+  }
+  // scales: one 64-row load per wave; waves 0-3 take the 256 activation rows
+  // (words 0-255 of the stage's scale area), waves 4-5 the 128 weight rows
+  // (words 256-383), waves 6-7 repeat the weight rows into words 384-511,
+  // which nothing reads, so that every wave waits on the same load count
+  const bool s_act = wave < 4;
+  const int srow = s_act ? 64 * wave + lane : 64 * (wave % 2) + lane;
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(s_act ? g.xs + m_base * kpb : g.ws + n_base * kpb),
+      static_cast<short>(0), (s_act ? kF8TM : kF8TN) * kpb, kF8BufferFlags);
+  const uint32_t soff = static_cast<uint32_t>(
+      (srow < (s_act ? rows_valid : cols_valid) ? srow : 0) * kpb);
+  const int sdst = (kF8TM + kF8TN) * kF8Row + 256 * wave;
+  constexpr int kWBase = kF8TM * kF8Row;                 // weight rows after the activations
+  constexpr int kSBase = (kF8TM + kF8TN) * kF8Row;       // scale words after the data
+
+  const int chunks = g.chunks;
+  auto issue = [&](int c, uint8_t *st) __attribute__((always_inline)) {
+    const int cc = c < chunks ? c : chunks - 1;  // padding steps reload the last one
+#pragma unroll
+    for (int i = 0; i < kF8ALoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          a_rsrc, (lds_void *)(st + (kF8ALoads * wave + i) * 1024), 16, aoff[i], kF8Row * cc, 0,
+          0);
+#pragma unroll
+    for (int i = 0; i < kF8WLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rsrc, (lds_void *)(st + kWBase + (kF8WLoads * wave + i) * 1024), 16, woff[i],
+          kF8Row * cc, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void *)(st + sdst), 4, soff, 4 * cc, 0,
+                                             0);
+  };
+
+  floatx4 acc[kF8MSub][kF8NSub];
+#pragma unroll
+  for (int i = 0; i < kF8MSub; ++i)
+#pragma unroll
+    for (int j = 0; j < kF8NSub; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint8_t *st) __attribute__((always_inline)) {
+    intx8 bq[kF8NSub];
+    int sb[kF8NSub];
+#pragma unroll
+    for (int j = 0; j < kF8NSub; ++j) {
+      const int row = wn * (16 * kF8NSub) + 16 * j + r;
+      const int key = (row >> 1) % 8;
+      const uint8_t *base = st + kWBase + row * kF8Row;
+      bq[j] = join(*reinterpret_cast<const uint4 *>(base + 16 * (grp ^ key)),
+                   *reinterpret_cast<const uint4 *>(base + 16 * ((4 + grp) ^ key)));
+      sb[j] = st[kSBase + 4 * (kF8TM + row) + grp];
+    }
+#pragma unroll
+    for (int i = 0; i < kF8MSub; ++i) {
+      const int row = wm * (16 * kF8MSub) + 16 * i + r;
+      const int key = (row >> 1) % 8;
+      const uint8_t *base = st + row * kF8Row;
+      const intx8 aq = join(*reinterpret_cast<const uint4 *>(base + 16 * (grp ^ key)),
+                            *reinterpret_cast<const uint4 *>(base + 16 * ((4 + grp) ^ key)));
+      const int sa = st[kSBase + 4 * row + grp];
+#pragma unroll
+      for (int j = 0; j < kF8NSub; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq, bq[j], acc[i][j], 0, 0,
+                                                                     0, sa, 0, sb[j]);
+    }
+  };
+
+  // Step c: wait until only step c + 1's loads are outstanding (loads retire
+  // in issue order), wait for this wave's LDS reads, barrier (step c is in LDS
+  // for every wave, and every wave is done with step c - 1's stage), refill
+  // that stage with step c + 2, multiply step c.  The step count is padded to
+  // a multiple of three; padding steps reload the last step and are not
+  // multiplied, which keeps every wait exact.
+  constexpr int kWait = 0x0F70 | (kF8Loads & 15) | ((kF8Loads >> 4) << 14);
+  auto step = [&](int c, const uint8_t *cur, uint8_t *far) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kWait);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    issue(c + 2, far);
+    if (c < chunks) compute(cur);
+  };
+  issue(0, stage0);
+  issue(1, stage1);
+  for (int c = 0; c < chunks; c += 3) {
+    step(c, stage0, stage2);
+    step(c + 1, stage1, stage0);
+    step(c + 2, stage2, stage1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding steps' loads
+
+  const bool full = rows_valid >= kF8TM && cols_valid >= kF8TN;
+#pragma unroll
+  for (int i = 0; i < kF8MSub; ++i)
+#pragma unroll
+    for (int j = 0; j < kF8NSub; ++j) {
+      const int64_t n = n_base + wn * (16 * kF8NSub) + 16 * j + r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = m_base + wm * (16 * kF8MSub) + 16 * i + 4 * grp + v;
+        if (full || (m < g.m && n < g.n)) g.y[m * g.n + n] = acc[i][j][v];
+      }
+    }
+}
+
+}  // namespace
+
+int64_t fp8_padded_k(int64_t k) { return (k + 127) / 128 * 128; }
+
+hipError_t launch_fp8_cache(const uint8_t *packed, int64_t n, int64_t k, uint32_t sign_bits,
+                            uint8_t *codes, uint8_t *scales, hipStream_t s) {
+  const int32_t kpb = static_cast<int32_t>(fp8_padded_k(k) / 32);
+  const int64_t threads = n * kpb;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp8_cache_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                     dim3(256), 0, s, packed, n, static_cast<int32_t>(k / 32), kpb, sign_bits,
+                     codebook(), codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_mxfp8(const uint16_t *x, int64_t m, int64_t k, uint8_t *codes,
+                            uint8_t *scales, hipStream_t s) {
+  const int32_t kpb = static_cast<int32_t>(fp8_padded_k(k) / 32);
+  const int64_t threads = m * kpb;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(act_mxfp8_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                     dim3(256), 0, s, x, m, static_cast<int32_t>(k / 32), kpb, codes, scales);
+  return hipGetLastError();
+}
+
+bool fp8_shape_fits(int64_t m, int64_t k, int64_t n) {
+  // 32-bit buffer offsets over one tile's 256 padded rows
+  return m >= 1 && n >= 1 && k >= 32 && fp8_padded_k(k) * kF8TM < (int64_t{1} << 31);
+}
+
+hipError_t launch_linear_fp8(const uint8_t *xq, const uint8_t *xs, int64_t m, int64_t k,
+                             const uint8_t *wq, const uint8_t *ws, int64_t n, float *y,
+                             hipStream_t s) {
+  if (!fp8_shape_fits(m, k, n)) return hipErrorInvalidValue;
+  F8Args g{};
+  g.xq = xq;
+  g.xs = xs;
+  g.wq = wq;
+  g.ws = ws;
+  g.y = y;
+  g.m = m;
+  g.n = n;
+  g.kp = fp8_padded_k(k);
+  g.kpb = static_cast<int32_t>(g.kp / 32);
+  g.chunks = static_cast<int32_t>(g.kp / 128);
+  if (m <= 64) {
+    const dim3 grid(static_cast<unsigned>((n + 15) / 16));
+    const dim3 block(64 * kF8SkWaves);
+    switch ((m + 15) / 16) {
+      case 1: hipLaunchKernelGGL(fp8_skinny_kernel<1>, grid, block, 0, s, g); break;
+      case 2: hipLaunchKernelGGL(fp8_skinny_kernel<2>, grid, block, 0, s, g); break;
+      case 3: hipLaunchKernelGGL(fp8_skinny_kernel<3>, grid, block, 0, s, g); break;
+      default: hipLaunchKernelGGL(fp8_skinny_kernel<4>, grid, block, 0, s, g); break;
+    }
+    return hipGetLastError();
+  }
+  g.tiles_m = static_cast<int32_t>((m + kF8TM - 1) / kF8TM);
+  g.tiles_n = static_cast<int32_t>((n + kF8TN - 1) / kF8TN);
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(g.tiles_m) * g.tiles_n));
+  hipLaunchKernelGGL(fp8_gemm_kernel, grid, dim3(64 * kF8Waves), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace tq4

@@ -188,6 +188,19 @@ hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_
                            int64_t n, const MoETile *tiles, const int32_t *n_tiles,
                            float *out, uint16_t *out16, uint32_t sign_bits, hipStream_t s);
 
+// fp8 weight cache (MXFP8: e4m3 codes, one E8M0 scale per 32 k), rows
+// padded to fp8_padded_k(k) (a multiple of 128) with zero codes and scales.
+int64_t fp8_padded_k(int64_t k);
+hipError_t launch_fp8_cache(const uint8_t *packed, int64_t n, int64_t k, uint32_t sign_bits,
+                            uint8_t *codes, uint8_t *scales, hipStream_t s);
+hipError_t launch_act_mxfp8(const uint16_t *x, int64_t m, int64_t k, uint8_t *codes,
+                            uint8_t *scales, hipStream_t s);
+bool fp8_shape_fits(int64_t m, int64_t k, int64_t n);
+// y = dequant(xq, xs) . dequant(wq, ws)^T, fp32.
+hipError_t launch_linear_fp8(const uint8_t *xq, const uint8_t *xs, int64_t m, int64_t k,
+                             const uint8_t *wq, const uint8_t *ws, int64_t n, float *y,
+                             hipStream_t s);
+
 // Streaming read of `bytes` (a multiple of 16) from a 16-byte aligned buffer.
 hipError_t launch_read_probe(const void *src, int64_t bytes, float *sink, hipStream_t s);
 

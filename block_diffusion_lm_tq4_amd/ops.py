@@ -171,6 +171,65 @@ def linear_epilogue_bf16(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
                         workspace, torch.bfloat16)
 
 
+def fp8_padded_k(k: int) -> int:
+    return (k + 127) // 128 * 128
+
+
+def fp8_cache(packed: torch.Tensor, sign_bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """packed [n, k/32, 20] -> the fp8 weight cache (flat uint8: codes [n][kp],
+    then scale bytes [n][kp/32]) (tq4_fp8_cache)."""
+    _cuda_contig(packed, "packed", torch.uint8)
+    _require(packed.dim() == 3 and packed.shape[2] == BLOCK_BYTES, "packed must be [n, k/32, 20]")
+    n, k = packed.shape[0], packed.shape[1] * BLOCK
+    size = int(lib().tq4_fp8_cache_size(n, k))
+    if out is None:
+        out = torch.empty(max(size, 16), dtype=torch.uint8, device=packed.device)
+    _cuda_contig(out, "out", torch.uint8)
+    _require(out.numel() >= size, "out is smaller than tq4_fp8_cache_size(n, k)")
+    check("tq4_fp8_cache", lib().tq4_fp8_cache(packed.data_ptr(), n, k, sign_bits & 0xFFFFFFFF,
+                                               out.data_ptr(), _stream(packed.device)))
+    return out
+
+
+def fp8_cache_views(cache: torch.Tensor, n: int, k: int) -> tuple[torch.Tensor, torch.Tensor]:
+    """(codes [n, kp], scales [n, kp/32]) views of a flat cache."""
+    kp = fp8_padded_k(k)
+    return cache[:n * kp].view(n, kp), cache[n * kp:n * kp + n * kp // 32].view(n, kp // 32)
+
+
+def act_mxfp8(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16 x [m, k] -> (codes [m, kp], scales [m, kp/32]) uint8 (tq4_act_mxfp8)."""
+    _cuda_contig(x, "x", torch.bfloat16)
+    m, k = x.shape
+    kp = fp8_padded_k(k)
+    codes = torch.empty((m, kp), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((m, kp // 32), dtype=torch.uint8, device=x.device)
+    check("tq4_act_mxfp8", lib().tq4_act_mxfp8(x.data_ptr(), m, k, codes.data_ptr(),
+                                               scales.data_ptr(), _stream(x.device)))
+    return codes, scales
+
+
+def linear_fp8(x: torch.Tensor, cache: torch.Tensor, n: int, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x . W^T from the fp8 cache of an [n, k] matrix, fp32 [m, n] (tq4_linear_fp8)."""
+    _cuda_contig(x, "x", torch.bfloat16)
+    _cuda_contig(cache, "cache", torch.uint8)
+    _require(x.dim() == 2, "x must be [m, k]")
+    m, k = x.shape
+    _require(cache.numel() >= int(lib().tq4_fp8_cache_size(n, k)), "cache too small for [n, k]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _cuda_contig(out, "out", torch.float32)
+    _require(tuple(out.shape) == (m, n), "out must be [m, n]")
+    need = int(lib().tq4_linear_fp8_workspace_size(m, k, n))
+    if workspace is None:
+        workspace = _WS.get(x.device, "linear_fp8", need)
+    check("tq4_linear_fp8", lib().tq4_linear_fp8(x.data_ptr(), m, k, cache.data_ptr(), n,
+                                                 out.data_ptr(), workspace.data_ptr(),
+                                                 workspace.numel(), _stream(x.device)))
+    return out
+
+
 def linear_rotated(xt: torch.Tensor, packed: torch.Tensor, out: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y = xt . Z_hat^T with xt = act_rht(x) already rotated (tq4_linear_rotated)."""

@@ -172,6 +172,61 @@ int tq4_linear_epilogue_bf16(const uint16_t *x_bf16, int64_t m, int64_t k,
                              uint16_t *y_bf16, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* ---- fp8 weight cache ----------------------------------------------------
+ * The card's proposed alternative (model card, Help wanted): decode the
+ * weights once into a resident fp8 copy, about 63 GB for both towers, so
+ * that no forward pass decodes.  Encoding (MXFP8): OCP e4m3 codes (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, subnormals, NaN only at 0x7F
+ * and 0xFF, largest 448) with one power-of-two scale 2^e per 32 consecutive
+ * k of a row -- the same 32-weight blocks -- stored as the E8M0 byte e + 127;
+ * e is the smallest integer in [-127, 127] with max|block| <= 448 * 2^e
+ * (e = -127 for an all-zero block), and an element v is stored as the e4m3
+ * code nearest to v / 2^e, ties to the even code, sign kept.  Rows are
+ * padded to kp = k rounded up to a multiple of 128 with zero codes and zero
+ * scale bytes, which add nothing to a product.  A cache of an [n, k] matrix
+ * is the codes [n][kp] followed by the scale bytes [n][kp/32]. */
+
+/* Bytes of the fp8 cache of an [n, k] matrix: n * kp + n * kp / 32 (0 if the
+ * sizes are invalid or empty). */
+size_t tq4_fp8_cache_size(int64_t n, int64_t k);
+
+/* Build the cache from a packed [n][k/32][20] matrix (device, 4-byte
+ * aligned): the decoded weights W_hat (rotation undone, fp64 arithmetic)
+ * encoded as above.  cache: device, 16-byte aligned, tq4_fp8_cache_size
+ * bytes.  The codes are exactly those of the rule above whenever the two
+ * half-block scales of each block are within a factor 2^12 of each other
+ * (then every sum of the inverse rotation is exact in fp64).  Offline, like
+ * tq4_pack.  Errors: TQ4_E_NULL, TQ4_E_SHAPE (negative sizes, k % 32 != 0,
+ * kp >= 2^23), TQ4_E_ALIGN, TQ4_E_DEVICE.  n == 0 or k == 0 is a no-op. */
+int tq4_fp8_cache(const uint8_t *packed, int64_t n, int64_t k, uint32_t sign_bits,
+                  uint8_t *cache, void *stream);
+
+/* Quantize bf16 activations [m, k] (device, 16-byte aligned) the same way:
+ * codes [m][kp] (device, 16-byte aligned) and scale bytes [m][kp/32]
+ * (device).  Non-finite inputs give unspecified codes.  Errors as
+ * tq4_fp8_cache. */
+int tq4_act_mxfp8(const uint16_t *x_bf16, int64_t m, int64_t k, uint8_t *codes,
+                  uint8_t *scales, void *stream);
+
+/* Workspace bytes for tq4_linear_fp8 (the quantized activations). */
+size_t tq4_linear_fp8_workspace_size(int64_t m, int64_t k, int64_t n);
+
+/* y[m, n] = sum_k xq[m, k] wq[n, k] with both operands dequantized from the
+ * fp8 encoding: x is quantized per call (tq4_act_mxfp8, into the workspace),
+ * the weights come from a cache built by tq4_fp8_cache; the product runs on
+ * the block-scaled fp8 MFMA with fp32 accumulation, deterministic.  Against
+ * the exact TQ4_1S product the fp8 rounding of both operands (at most 2^-4
+ * relative each) dominates the error.
+ *   x_bf16 : [m, k] bf16 bit patterns, device, 16-byte aligned
+ *   cache  : from tq4_fp8_cache for this [n, k], device, 16-byte aligned
+ *   y      : [m, n] fp32, device, 4-byte aligned, overwritten
+ *   workspace : tq4_linear_fp8_workspace_size(m, k, n) bytes, 256-byte
+ *               aligned
+ * Errors: as tq4_linear.  k == 0 writes zeros. */
+int tq4_linear_fp8(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *cache,
+                   int64_t n, float *y, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
 /* Stable bucketing of the t*topk (token, slot) pairs by expert, the routing
  * step of the sync-free MoE (model card, Running it; 128 experts, top-6 in
  * The model underneath).  Pair p = token * topk + slot.

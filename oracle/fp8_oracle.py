@@ -87,21 +87,26 @@ def e4m3_round(v: np.ndarray) -> np.ndarray:
 
 
 def e8m0_exponent(amax: np.ndarray) -> np.ndarray:
-    """Smallest e in [-127, 127] with amax <= 448 * 2^e (-127 for amax = 0)."""
-    amax = np.asarray(amax, dtype=np.float64)
-    out = np.full(amax.shape, -127, dtype=np.int64)
-    flat_a = amax.reshape(-1)
-    flat_o = out.reshape(-1)
-    for i, a in enumerate(flat_a):
-        if a == 0.0:
-            continue
-        e = int(np.floor(np.log2(a / E4M3_MAX)))
-        while a > np.ldexp(E4M3_MAX, e):           # too small: raise
-            e += 1
-        while e > -127 and a <= np.ldexp(E4M3_MAX, e - 1):  # not the smallest: lower
-            e -= 1
-        flat_o[i] = max(-127, min(127, e))
-    return out
+    """Smallest e in [-127, 127] with amax <= 448 * 2^e (-127 for amax = 0).
+
+    A first guess from log2, then exact power-of-two comparisons move each e
+    up while amax > 448 * 2^e and down while amax <= 448 * 2^(e - 1)."""
+    a = np.asarray(amax, dtype=np.float64)
+    nz = a > 0
+    with np.errstate(divide="ignore"):
+        e = np.where(nz, np.floor(np.log2(np.where(nz, a, 1.0) / E4M3_MAX)), -127.0)
+    e = e.astype(np.int64)
+    while True:
+        up = nz & (a > np.ldexp(E4M3_MAX, e))
+        if not up.any():
+            break
+        e = e + up
+    while True:
+        down = nz & (e > -127) & (a <= np.ldexp(E4M3_MAX, e - 1))
+        if not down.any():
+            break
+        e = e - down
+    return np.clip(e, -127, 127)
 
 
 def mx_quantize(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

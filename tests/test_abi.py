@@ -166,6 +166,44 @@ def test_linear_epilogue_bf16_argument_errors(L):
     assert call(m=0) == OK
 
 
+def test_fp8_argument_errors(L):
+    # sizes: codes n * kp then scale bytes n * kp / 32, kp = k rounded up to 128
+    assert L.tq4_fp8_cache_size(8192, 2688) == 8192 * 2688 + 8192 * 84
+    assert L.tq4_fp8_cache_size(10, 96) == 10 * 128 + 10 * 4
+    assert L.tq4_fp8_cache_size(10, 33) == 0 and L.tq4_fp8_cache_size(-1, 64) == 0
+    assert L.tq4_linear_fp8_workspace_size(16, 2688, 8192) >= 16 * 2688 + 16 * 84
+    assert L.tq4_linear_fp8_workspace_size(0, 2688, 8192) == 0
+    assert L.tq4_fp8_cache(FAKE, 8, 96, 0, None, None) == E_NULL
+    assert L.tq4_fp8_cache(None, 8, 96, 0, FAKE, None) == E_NULL
+    assert L.tq4_fp8_cache(FAKE, 8, 95, 0, FAKE, None) == E_SHAPE
+    assert L.tq4_fp8_cache(FAKE + 2, 8, 96, 0, FAKE, None) == E_ALIGN
+    assert L.tq4_fp8_cache(FAKE, 8, 96, 0, FAKE + 4, None) == E_ALIGN
+    assert L.tq4_fp8_cache(FAKE, 0, 96, 0, None, None) == OK
+    assert L.tq4_act_mxfp8(FAKE, 4, 64, FAKE, None, None) == E_NULL
+    assert L.tq4_act_mxfp8(FAKE + 2, 4, 64, FAKE, FAKE, None) == E_ALIGN
+    assert L.tq4_act_mxfp8(FAKE, 4, 64, FAKE + 8, FAKE, None) == E_ALIGN
+    assert L.tq4_act_mxfp8(FAKE, 4, 48, FAKE, FAKE, None) == E_SHAPE
+    ws = L.tq4_linear_fp8_workspace_size(100, 2688, 8192)
+
+    def call(**kw):
+        a = dict(dict(x=FAKE, m=100, k=2688, c=FAKE, n=8192, y=FAKE, ws=FAKE, wsb=ws), **kw)
+        return L.tq4_linear_fp8(a["x"], a["m"], a["k"], a["c"], a["n"], a["y"], a["ws"],
+                                a["wsb"], None)
+
+    assert call(k=2690) == E_SHAPE
+    assert call(m=-1) == E_SHAPE
+    assert call(x=None) == E_NULL
+    assert call(c=None) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(x=MIS) == E_ALIGN
+    assert call(c=FAKE + 4) == E_ALIGN
+    assert call(y=FAKE + 2) == E_ALIGN
+    assert call(ws=None) == E_WS
+    assert call(wsb=ws - 1) == E_WS
+    assert call(ws=FAKE + 16) == E_ALIGN
+    assert call(m=0) == OK and call(n=0) == OK
+
+
 def test_moe_argument_errors(L):
     ws = L.tq4_moe_workspace_size(16, 6, 128, 1856, 2688)
     assert ws > 0
