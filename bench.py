@@ -11,8 +11,9 @@ its weights from HBM.  Inputs are resident in HBM before timing starts.
 Extra legs in the same JSON line: the M=4096 prefill projection (TFLOP/s,
 Student-t weights) and the 128-expert top-6 MoE layer at 16 and 1024 tokens
 (uniform and Zipf routing), each timed the same way, with its own roofline;
-the offline quantizer's throughput; and the fused bias + residual tail
-(tq4_linear_epilogue) at M=16 and M=4096 against the plain call.
+the offline quantizer's throughput; the fused bias + residual tail
+(tq4_linear_epilogue) at M=16 and M=4096 against the plain call; and the fp8
+weight-cache variant (tq4_fp8_cache / tq4_linear_fp8) on the same two shapes.
 
 `roofline` is for the dominant kernel of the headline step: at M=16 the whole
 tq4_linear call is one kernel (rotation fused), so its time per launch is the
@@ -37,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, TFLOP/s
 
 
 def log(*a):
@@ -226,6 +228,45 @@ def epilogue_leg(torch, np, ops, I, wl, steps, warmup, copies, dev, sb):
             "fused_bf16_stream_us": round(ms_h * 1e3, 2)}
 
 
+def fp8_leg(torch, np, ops, I, wl, steps, warmup, copies, dev, sb):
+    """The fp8 weight-cache variant on one dense workload: the one-time cache
+    build, a step (activation quantization + product, tq4_linear_fp8) and the
+    product alone (tq4_linear_fp8_quantized), the cache rotating over
+    `copies` distinct copies."""
+    w = I.weights(wl.n, wl.k, wl.weights)
+    packed = ops.pack(torch.from_numpy(w).to(dev), sb)
+    del w
+    cache = ops.fp8_cache(packed, sb)
+    ms_build = time_loop(torch, lambda i: ops.fp8_cache(packed, sb, out=cache), 5, 1)
+    stack = [cache] + [cache.clone() for _ in range(copies - 1)]
+    x = bf16_dev(torch, np, I.activations_bf16(wl.m, wl.k), dev)
+    y = torch.empty((wl.m, wl.n), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(ops.linear_fp8_workspace_size(wl.m, wl.k, wl.n), 256),
+                     dtype=torch.uint8, device=dev)
+    codes, scales = ops.act_mxfp8(x)
+    ms_step = time_loop(torch, lambda i: ops.linear_fp8(x, stack[i % copies], wl.n, out=y,
+                                                        workspace=ws), steps, warmup)
+    ms_kernel = time_loop(torch, lambda i: ops.linear_fp8_quantized(
+        codes, scales, wl.k, stack[i % copies], wl.n, out=y), steps, warmup)
+    r = dict(ms_build=ms_build, ms_step=ms_step, ms_kernel=ms_kernel, cache_bytes=cache.numel(),
+             flops=2.0 * wl.m * wl.n * wl.k)
+    if wl.m > 16:
+        # context: the vendor BLAS fp8 GEMM (torch._scaled_mm -> hipBLASLt), e4m3 operands
+        # with per-tensor scales, fp32 out, same shape
+        try:
+            a8 = torch.randn((wl.m, wl.k), device=dev).to(torch.float8_e4m3fn)
+            b8 = torch.randn((wl.n, wl.k), device=dev).to(torch.float8_e4m3fn)
+            one = torch.ones((), device=dev)
+            c32 = torch.empty((wl.m, wl.n), dtype=torch.float32, device=dev)
+            torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.float32)
+            r["ms_fp8_blas"] = time_loop(torch, lambda i: torch._scaled_mm(
+                a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.float32, out=c32),
+                steps, warmup)
+        except Exception as e:  # the library path is optional context
+            r["fp8_blas_error"] = f"{type(e).__name__}: {str(e)[:120]}"
+    return r
+
+
 def pack_leg(torch, np, ops, I, steps, warmup, dev, sb, n=8192, k=2688):
     """Offline quantizer throughput (tq4_pack_bf16 and tq4_pack) on one
     denoiser-projection-sized matrix, weights resident on the device."""
@@ -282,7 +323,7 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=48)
     ap.add_argument("--legs", default="all",
                     help="all | none | comma list of dense_m4096_t3,moe_t16,"
-                         "moe_t1024_uniform,moe_t1024_zipf,pack,epilogue")
+                         "moe_t1024_uniform,moe_t1024_zipf,pack,epilogue,fp8")
     ap.add_argument("--only", default=None,
                     help="profile helper: run just this workload (no JSON contract)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -310,6 +351,12 @@ def main() -> int:
     sb = I.sign_bits()
 
     if args.only:
+        if args.only.startswith("fp8_"):
+            wl = I.WORKLOADS[args.only[4:]]
+            r = fp8_leg(torch, np, ops, I, wl, args.steps, args.warmup,
+                        24 if wl.m <= 16 else 2, dev, sb)
+            log(args.only, json.dumps(r))
+            return 0
         wl = I.WORKLOADS[args.only]
         if args.only.startswith("dense"):
             r = dense_leg(torch, np, ops, I, wl, args.steps, args.warmup, args.copies, dev, sb)
@@ -348,7 +395,7 @@ def main() -> int:
     legs = {}
     names = ([] if args.legs == "none" else
              ["dense_m4096_t3", "moe_t16", "moe_t1024_uniform", "moe_t1024_zipf", "pack",
-              "epilogue"]
+              "epilogue", "fp8"]
              if args.legs == "all" else args.legs.split(","))
     experts = None
     for name in names:
@@ -356,6 +403,45 @@ def main() -> int:
             log("pack: running")
             legs[name] = pack_leg(torch, np, ops, I, max(5, args.steps // 20), 2, dev, sb)
             log(name, json.dumps(legs[name]))
+            continue
+        if name == "fp8":
+            log("fp8: running")
+            q16 = fp8_leg(torch, np, ops, I, I.WORKLOADS["dense_m16"], max(5, args.steps // 2),
+                          max(2, args.warmup // 2), 24, dev, sb)
+            q4k = fp8_leg(torch, np, ops, I, I.WORKLOADS["dense_m4096_t3"],
+                          max(5, args.steps // 20), max(2, args.warmup // 10), 2, dev, sb)
+            k16 = q16["cache_bytes"] / (q16["ms_kernel"] * 1e-3) / 1e9
+            t4k = q4k["flops"] / (q4k["ms_kernel"] * 1e-3) / 1e12
+            leg = {
+                "dense_m16": {
+                    "step_us": round(q16["ms_step"] * 1e3, 2),
+                    "product_us": round(q16["ms_kernel"] * 1e3, 2),
+                    "tq4_step_us": round(r["ms_step"] * 1e3, 2),
+                    "cache_bytes": q16["cache_bytes"],
+                    "cache_build_us": round(q16["ms_build"] * 1e3, 1),
+                    "roofline": {"bound": "hbm", "achieved": round(k16, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(k16 / HBM_PEAK_GBS, 4),
+                                 "kernel": "fp8_skinny_kernel<1> (tq4_linear_fp8_quantized), "
+                                           "algorithmic bytes = fp8 cache (codes + scales)"}},
+                "dense_m4096_t3": {
+                    "step_ms": round(q4k["ms_step"], 4),
+                    "product_ms": round(q4k["ms_kernel"], 4),
+                    "TFLOP/s": round(t4k, 1),
+                    "roofline": {"bound": "mfma", "achieved": round(t4k, 1),
+                                 "peak": MFMA_F8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(t4k / MFMA_F8_PEAK_TFLOPS, 4),
+                                 "kernel": "fp8_gemm_kernel (tq4_linear_fp8_quantized), "
+                                           "2*M*N*K flops per launch"}}}
+            if "ms_fp8_blas" in q4k:
+                bt = q4k["flops"] / (q4k["ms_fp8_blas"] * 1e-3) / 1e12
+                leg["dense_m4096_t3"]["context_fp8_blas"] = {
+                    "what": "torch._scaled_mm (hipBLASLt) e4m3 x e4m3 -> fp32, per-tensor "
+                            "scales, same shape",
+                    "TFLOP/s": round(bt, 1), "ours_over_blas": round(t4k / bt, 4)}
+            elif "fp8_blas_error" in q4k:
+                leg["dense_m4096_t3"]["context_fp8_blas"] = {"error": q4k["fp8_blas_error"]}
+            legs[name] = leg
+            log(name, json.dumps(leg))
             continue
         if name == "epilogue":
             log("epilogue: running")

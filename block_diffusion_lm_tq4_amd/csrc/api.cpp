@@ -370,6 +370,22 @@ int tq4_linear_fp8(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *
       tq4::launch_linear_fp8(xq, xs, m, k, cache, cache + n * kp, n, y, s));
 }
 
+int tq4_linear_fp8_quantized(const uint8_t *x_codes, const uint8_t *x_scales, int64_t m,
+                             int64_t k, const uint8_t *cache, int64_t n, float *y,
+                             void *stream) {
+  if (!fp8_sizes_ok(m, k) || n < 0) return TQ4_E_SHAPE;
+  if (m == 0 || n == 0) return TQ4_OK;
+  if (y == nullptr) return TQ4_E_NULL;
+  if (!aligned(y, 4)) return TQ4_E_ALIGN;
+  hipStream_t s = as_stream(stream);
+  if (k == 0) return device_status(tq4::launch_fill_zero(y, m * n, s));
+  if (x_codes == nullptr || x_scales == nullptr || cache == nullptr) return TQ4_E_NULL;
+  if (!aligned(x_codes, 16) || !aligned(x_scales, 4) || !aligned(cache, 16)) return TQ4_E_ALIGN;
+  const int64_t kp = tq4::fp8_padded_k(k);
+  return device_status(
+      tq4::launch_linear_fp8(x_codes, x_scales, m, k, cache, cache + n * kp, n, y, s));
+}
+
 int tq4_read_probe(const void *src, int64_t bytes, float *sink, void *stream) {
   if (bytes < 0 || bytes % 16 != 0) return TQ4_E_SHAPE;
   if (bytes == 0) return TQ4_OK;

@@ -197,6 +197,10 @@ def fp8_cache_views(cache: torch.Tensor, n: int, k: int) -> tuple[torch.Tensor, 
     return cache[:n * kp].view(n, kp), cache[n * kp:n * kp + n * kp // 32].view(n, kp // 32)
 
 
+def linear_fp8_workspace_size(m: int, k: int, n: int) -> int:
+    return int(lib().tq4_linear_fp8_workspace_size(m, k, n))
+
+
 def act_mxfp8(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     """bf16 x [m, k] -> (codes [m, kp], scales [m, kp/32]) uint8 (tq4_act_mxfp8)."""
     _cuda_contig(x, "x", torch.bfloat16)
@@ -227,6 +231,29 @@ def linear_fp8(x: torch.Tensor, cache: torch.Tensor, n: int, out: torch.Tensor |
     check("tq4_linear_fp8", lib().tq4_linear_fp8(x.data_ptr(), m, k, cache.data_ptr(), n,
                                                  out.data_ptr(), workspace.data_ptr(),
                                                  workspace.numel(), _stream(x.device)))
+    return out
+
+
+def linear_fp8_quantized(x_codes: torch.Tensor, x_scales: torch.Tensor, k: int,
+                         cache: torch.Tensor, n: int,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """y from activations already quantized by act_mxfp8 (tq4_linear_fp8_quantized)."""
+    _cuda_contig(x_codes, "x_codes", torch.uint8)
+    _cuda_contig(x_scales, "x_scales", torch.uint8)
+    _cuda_contig(cache, "cache", torch.uint8)
+    m = x_codes.shape[0]
+    kp = fp8_padded_k(k)
+    _require(tuple(x_codes.shape) == (m, kp) and tuple(x_scales.shape) == (m, kp // 32),
+             "x_codes must be [m, kp] and x_scales [m, kp/32]")
+    _require(cache.numel() >= int(lib().tq4_fp8_cache_size(n, k)), "cache too small for [n, k]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x_codes.device)
+    _cuda_contig(out, "out", torch.float32)
+    _require(tuple(out.shape) == (m, n), "out must be [m, n]")
+    check("tq4_linear_fp8_quantized",
+          lib().tq4_linear_fp8_quantized(x_codes.data_ptr(), x_scales.data_ptr(), m, k,
+                                         cache.data_ptr(), n, out.data_ptr(),
+                                         _stream(x_codes.device)))
     return out
 
 

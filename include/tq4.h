@@ -227,6 +227,14 @@ int tq4_linear_fp8(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *
                    int64_t n, float *y, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/* tq4_linear_fp8 with the activations already quantized by tq4_act_mxfp8
+ * (x_codes [m][kp], device, 16-byte aligned; x_scales [m][kp/32], device,
+ * 4-byte aligned), so one quantization can serve several projections of the
+ * same input.  No workspace.  Errors as tq4_linear_fp8. */
+int tq4_linear_fp8_quantized(const uint8_t *x_codes, const uint8_t *x_scales, int64_t m,
+                             int64_t k, const uint8_t *cache, int64_t n, float *y,
+                             void *stream);
+
 /* Stable bucketing of the t*topk (token, slot) pairs by expert, the routing
  * step of the sync-free MoE (model card, Running it; 128 experts, top-6 in
  * The model underneath).  Pair p = token * topk + slot.

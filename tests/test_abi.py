@@ -202,6 +202,12 @@ def test_fp8_argument_errors(L):
     assert call(wsb=ws - 1) == E_WS
     assert call(ws=FAKE + 16) == E_ALIGN
     assert call(m=0) == OK and call(n=0) == OK
+    q = L.tq4_linear_fp8_quantized
+    assert q(FAKE, FAKE, 100, 2688, FAKE, 8192, None, None) == E_NULL
+    assert q(None, FAKE, 100, 2688, FAKE, 8192, FAKE, None) == E_NULL
+    assert q(FAKE, FAKE + 2, 100, 2688, FAKE, 8192, FAKE, None) == E_ALIGN
+    assert q(FAKE + 8, FAKE, 100, 2688, FAKE, 8192, FAKE, None) == E_ALIGN
+    assert q(FAKE, FAKE, 100, 2690, FAKE, 8192, FAKE, None) == E_SHAPE
 
 
 def test_moe_argument_errors(L):

@@ -145,6 +145,16 @@ def test_linear_fp8_prefill_m4096_sampled_rows(dev):
     assert np.isfinite(y).all()
 
 
+@pytest.mark.parametrize("m", [16, 300])
+def test_linear_fp8_quantized_equals_linear_fp8(dev, m):
+    _, cache = _cache(dev, 520, 2688, seed=7)
+    x = _bf16(I.activations_bf16(m, 2688, seed=3), dev)
+    codes, scales = _ops().act_mxfp8(x)
+    a = _ops().linear_fp8(x, cache, 520)
+    b = _ops().linear_fp8_quantized(codes, scales, 2688, cache, 520)
+    assert torch.equal(a, b)
+
+
 def test_linear_fp8_deterministic_and_k0(dev):
     _, cache = _cache(dev, 300, 2688, seed=5)
     for m in (16, 300):
