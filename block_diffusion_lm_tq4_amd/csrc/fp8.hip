@@ -357,37 +357,32 @@ __global__ __launch_bounds__(64 * kF8Waves) void fp8_gemm_kernel(F8Args g) {
   const int kp = static_cast<int>(g.kp);
   const int kpb = g.kpb;
 
-  // data: rows past the matrix read row 0 (their results are not stored)
+  // Each buffer's range ends at the matrix's last row, so a load of a row
+  // past it reads zeros without touching memory (those rows are not stored).
+  // Piece p holds rows 8p .. 8p + 7; its key (row / 2) % 8 is (lane / 16) ^
+  // (4 * (p % 2)), so a lane needs one offset for even and one for odd
+  // pieces; 8p rows and the step go in the scalar offset.
+  const int64_t a_rows = rows_valid < kF8TM ? rows_valid : kF8TM;
+  const int64_t w_rows = cols_valid < kF8TN ? cols_valid : kF8TN;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(g.xq + m_base * g.kp), static_cast<short>(0), kF8TM * kp,
-      kF8BufferFlags);
+      const_cast<uint8_t *>(g.xq + m_base * g.kp), static_cast<short>(0),
+      static_cast<int>(a_rows * kp), kF8BufferFlags);
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(g.wq + n_base * g.kp), static_cast<short>(0), kF8TN * kp,
-      kF8BufferFlags);
-  uint32_t aoff[kF8ALoads], woff[kF8WLoads];
-#pragma unroll
-  for (int i = 0; i < kF8ALoads; ++i) {
-    const int row = 8 * (kF8ALoads * wave + i) + lane / 8;
-    const int piece = (lane % 8) ^ ((row >> 1) % 8);
-    aoff[i] = static_cast<uint32_t>((row < rows_valid ? row : 0) * kp + 16 * piece);
-  }
-#pragma unroll
-  for (int i = 0; i < kF8WLoads; ++i) {
-    const int row = 8 * (kF8WLoads * wave + i) + lane / 8;
-    const int piece = (lane % 8) ^ ((row >> 1) % 8);
-    woff[i] = static_cast<uint32_t>((row < cols_valid ? row : 0) * kp + 16 * piece);
-  }
+      const_cast<uint8_t *>(g.wq + n_base * g.kp), static_cast<short>(0),
+      static_cast<int>(w_rows * kp), kF8BufferFlags);
+  const int key0 = (lane % 8) ^ (lane / 16);
+  const uint32_t voff_even = static_cast<uint32_t>((lane / 8) * kp + 16 * key0);
+  const uint32_t voff_odd = static_cast<uint32_t>((lane / 8) * kp + 16 * (key0 ^ 4));
   // scales: one 64-row load per wave; waves 0-3 take the 256 activation rows
   // (words 0-255 of the stage's scale area), waves 4-5 the 128 weight rows
   // (words 256-383), waves 6-7 repeat the weight rows into words 384-511,
   // which nothing reads, so that every wave waits on the same load count
   const bool s_act = wave < 4;
-  const int srow = s_act ? 64 * wave + lane : 64 * (wave % 2) + lane;
+  const int s_row0 = s_act ? 64 * wave : 64 * (wave % 2);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(s_act ? g.xs + m_base * kpb : g.ws + n_base * kpb),
-      static_cast<short>(0), (s_act ? kF8TM : kF8TN) * kpb, kF8BufferFlags);
-  const uint32_t soff = static_cast<uint32_t>(
-      (srow < (s_act ? rows_valid : cols_valid) ? srow : 0) * kpb);
+      static_cast<short>(0), static_cast<int>((s_act ? a_rows : w_rows) * kpb), kF8BufferFlags);
+  const uint32_t soff = static_cast<uint32_t>(lane * kpb);
   const int sdst = (kF8TM + kF8TN) * kF8Row + 256 * wave;
   constexpr int kWBase = kF8TM * kF8Row;                 // weight rows after the activations
   constexpr int kSBase = (kF8TM + kF8TN) * kF8Row;       // scale words after the data
@@ -396,17 +391,21 @@ __global__ __launch_bounds__(64 * kF8Waves) void fp8_gemm_kernel(F8Args g) {
   auto issue = [&](int c, uint8_t *st) __attribute__((always_inline)) {
     const int cc = c < chunks ? c : chunks - 1;  // padding steps reload the last one
 #pragma unroll
-    for (int i = 0; i < kF8ALoads; ++i)
+    for (int i = 0; i < kF8ALoads; ++i) {
+      const int piece = kF8ALoads * wave + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc, (lds_void *)(st + (kF8ALoads * wave + i) * 1024), 16, aoff[i], kF8Row * cc, 0,
-          0);
+          a_rsrc, (lds_void *)(st + piece * 1024), 16, piece % 2 ? voff_odd : voff_even,
+          8 * piece * kp + kF8Row * cc, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < kF8WLoads; ++i)
+    for (int i = 0; i < kF8WLoads; ++i) {
+      const int piece = kF8WLoads * wave + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          w_rsrc, (lds_void *)(st + kWBase + (kF8WLoads * wave + i) * 1024), 16, woff[i],
-          kF8Row * cc, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void *)(st + sdst), 4, soff, 4 * cc, 0,
-                                             0);
+          w_rsrc, (lds_void *)(st + kWBase + piece * 1024), 16, piece % 2 ? voff_odd : voff_even,
+          8 * piece * kp + kF8Row * cc, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void *)(st + sdst), 4, soff,
+                                             s_row0 * kpb + 4 * cc, 0, 0);
   };
 
   floatx4 acc[kF8MSub][kF8NSub];
