@@ -421,7 +421,7 @@ def main() -> int:
                     "cache_build_us": round(q16["ms_build"] * 1e3, 1),
                     "roofline": {"bound": "hbm", "achieved": round(k16, 1), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(k16 / HBM_PEAK_GBS, 4),
-                                 "kernel": "fp8_skinny_kernel<1> (tq4_linear_fp8_quantized), "
+                                 "kernel": "fp8_stream_kernel (tq4_linear_fp8_quantized), "
                                            "algorithmic bytes = fp8 cache (codes + scales)"}},
                 "dense_m4096_t3": {
                     "step_ms": round(q4k["ms_step"], 4),

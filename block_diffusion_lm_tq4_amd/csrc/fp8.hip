@@ -302,6 +302,132 @@ __global__ __launch_bounds__(64 * kF8SkWaves) void fp8_skinny_kernel(F8Args g) {
   }
 }
 
+// M <= 16, kp <= 3072: one workgroup of 8 waves per 32 output columns.  The
+// 16 quantized activation rows (codes and scale words) go to LDS once, and
+// wave w streams the weights of column tile w / 4 for the 128-k steps
+// c = w % 4, w % 4 + 4, ... (at most six): every load -- coalesced 1 KB
+// LDS-direct pieces of 8 rows x 128 bytes -- is issued before the first
+// product, so the whole workgroup's share (about 100 KB) is in flight at
+// once.  LDS rows of 128 bytes use the XOR swizzle of the large kernel; the
+// four partial sums of a column tile are added in wave order.
+constexpr int kF8BufferFlags = 0x00020000;
+constexpr int kF8StWaves = 8;
+constexpr int kF8StSteps = 6;                    // 128-k steps per wave at most
+constexpr int kF8StMaxKp = 4 * kF8StSteps * 128;  // 3072
+constexpr int kF8StX = 16 * kF8StMaxKp;           // activation codes, [step][row][128]
+constexpr int kF8StXs = 16 * (kF8StMaxKp / 32);   // activation scale bytes, [row][kpb]
+constexpr int kF8StW = kF8StSteps * 16 * 128;     // one wave's weight steps, [step][row][128]
+
+__global__ __launch_bounds__(64 * kF8StWaves) void fp8_stream_kernel(F8Args g) {
+  __shared__ __attribute__((aligned(16))) uint8_t xbuf[kF8StX];
+  __shared__ __attribute__((aligned(16))) uint8_t xsbuf[kF8StXs];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf[kF8StWaves][kF8StW];
+  // two 64-lane scale loads per wave: 512 bytes, of which steps 0..5 use 384
+  __shared__ __attribute__((aligned(16))) uint8_t wsbuf[kF8StWaves][512];
+  __shared__ floatx4 red[kF8StWaves][64];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int r = lane % 16;
+  const int grp = lane / 16;
+  const int kp = static_cast<int>(g.kp);
+  const int kpb = g.kpb;
+  const int chunks = g.chunks;
+  const int ntile = wave / 4;
+  const int ks = wave % 4;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 32 + 16 * ntile;
+
+  // rows past m and past n read zeros through the buffer ranges
+  const int64_t m_rows = g.m < 16 ? g.m : 16;
+  const int64_t n_rows = g.n - n0 < 16 ? (g.n - n0 > 0 ? g.n - n0 : 0) : 16;
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.xq), static_cast<short>(0), static_cast<int>(m_rows * kp),
+      kF8BufferFlags);
+  const __amdgpu_buffer_rsrc_t xs_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.xs), static_cast<short>(0), static_cast<int>(m_rows * kpb),
+      kF8BufferFlags);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.wq + n0 * g.kp), static_cast<short>(0),
+      static_cast<int>(n_rows * kp), kF8BufferFlags);
+  const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.ws + n0 * kpb), static_cast<short>(0),
+      static_cast<int>(n_rows * kpb), kF8BufferFlags);
+  // piece = 8 rows x 128 bytes of one step; key of row (8 h + l / 8) is
+  // (l / 16) ^ 4 h for h = 0, 1
+  const int key0 = (lane % 8) ^ (lane / 16);
+  const uint32_t voff0 = static_cast<uint32_t>((lane / 8) * kp + 16 * key0);
+  const uint32_t voff1 = static_cast<uint32_t>((lane / 8 + 8) * kp + 16 * (key0 ^ 4));
+
+  // activations: 2 pieces per step, spread over the waves
+  for (int piece = wave; piece < 2 * chunks; piece += kF8StWaves) {
+    const int c = piece / 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lds_void *)(xbuf + piece * 1024), 16,
+                                             piece % 2 ? voff1 : voff0, 128 * c, 0, 0);
+  }
+  // activation scale bytes: 16 rows x kpb, 64 words per load
+  for (int wd = 64 * wave; wd < 16 * kpb / 4; wd += 64 * kF8StWaves) {
+    const int w = wd + lane;
+    const int row = (4 * w) / kpb;
+    const int col = (4 * w) % kpb;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xs_rsrc, (lds_void *)(xsbuf + 4 * wd), 4,
+                                             static_cast<uint32_t>(row * kpb + col), 0, 0, 0);
+  }
+  // this wave's weight steps and their scale words (lane l: row l % 16 of
+  // step ks + 4 (l / 16); two loads cover six steps)
+  int nsteps = 0;
+#pragma unroll
+  for (int s = 0; s < kF8StSteps; ++s) {
+    const int c = ks + 4 * s;
+    if (c < chunks) {
+      nsteps = s + 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void *)(wbuf[wave] + s * 2048), 16,
+                                               voff0, 128 * c, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void *)(wbuf[wave] + s * 2048 + 1024),
+                                               16, voff1, 128 * c, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (ks + 16 * t < chunks)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ws_rsrc, (lds_void *)(wsbuf[wave] + 256 * t), 4,
+          static_cast<uint32_t>(r * kpb + 16 * grp), 4 * (ks + 16 * t), 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int key = (r >> 1) % 8;
+  for (int s = 0; s < nsteps; ++s) {
+    const int c = ks + 4 * s;
+    const uint8_t *xr = xbuf + c * 2048 + r * 128;
+    const uint8_t *wr = wbuf[wave] + s * 2048 + r * 128;
+    const intx8 aq = join(*reinterpret_cast<const uint4 *>(xr + 16 * (grp ^ key)),
+                          *reinterpret_cast<const uint4 *>(xr + 16 * ((4 + grp) ^ key)));
+    const intx8 bq = join(*reinterpret_cast<const uint4 *>(wr + 16 * (grp ^ key)),
+                          *reinterpret_cast<const uint4 *>(wr + 16 * ((4 + grp) ^ key)));
+    const int sa = xsbuf[r * kpb + 4 * c + grp];
+    const int sb = wsbuf[wave][256 * (s / 4) + 64 * (s % 4) + 4 * r + grp];
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq, bq, acc, 0, 0, 0, sa, 0, sb);
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave % 4 == 0) {
+    floatx4 sum = red[wave][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) sum += red[wave + w][lane];
+    const int64_t n = n0 + r;
+    if (n < g.n) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = 4 * grp + v;
+        if (m < g.m) g.y[m * g.n + n] = sum[v];
+      }
+    }
+  }
+}
+
 // Large M: 256 x 128 output tile per workgroup of 8 waves (4 along m, 2
 // along n; each 64 x 64 as 4 x 4 tiles of 16 x 16), two waves per SIMD.  Per
 // 128-k step the tile's activation rows (256 x 128 bytes), weight rows
@@ -320,7 +446,6 @@ constexpr int kF8ALoads = kF8TM * kF8Row / 1024 / kF8Waves;  // 4
 constexpr int kF8WLoads = kF8TN * kF8Row / 1024 / kF8Waves;  // 2
 constexpr int kF8Loads = kF8ALoads + kF8WLoads + 1;           // + one scale load
 constexpr int kF8Stage = (kF8TM + kF8TN) * kF8Row + 512 * 4;  // data, then 512 scale words
-constexpr int kF8BufferFlags = 0x00020000;
 
 __global__ __launch_bounds__(64 * kF8Waves) void fp8_gemm_kernel(F8Args g) {
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kF8Stage];
@@ -523,6 +648,11 @@ hipError_t launch_linear_fp8(const uint8_t *xq, const uint8_t *xs, int64_t m, in
   g.kp = fp8_padded_k(k);
   g.kpb = static_cast<int32_t>(g.kp / 32);
   g.chunks = static_cast<int32_t>(g.kp / 128);
+  if (m <= 16 && g.kp <= kF8StMaxKp) {
+    hipLaunchKernelGGL(fp8_stream_kernel, dim3(static_cast<unsigned>((n + 31) / 32)),
+                       dim3(64 * kF8StWaves), 0, s, g);
+    return hipGetLastError();
+  }
   if (m <= 64) {
     const dim3 grid(static_cast<unsigned>((n + 15) / 16));
     const dim3 block(64 * kF8SkWaves);

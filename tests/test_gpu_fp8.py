@@ -117,6 +117,8 @@ def _check_fp8_product(y, x, rc, rs, what):
 
 @pytest.mark.parametrize("m,k,n", [
     (16, 2688, 8192), (1, 32, 1), (5, 96, 17), (16, 160, 129), (33, 256, 100),
+    # m <= 16 streaming kernel at its k limit (kp 3072) and just past it
+    (16, 3072, 64), (7, 2944, 100), (16, 3200, 40), (3, 4096, 33),
     (64, 512, 300), (48, 2688, 40),
     # 256 x 128 tiles: ragged m, n and k, steps not a multiple of three
     (65, 256, 130), (300, 160, 200), (512, 2688, 1024), (257, 384, 129),
