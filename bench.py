@@ -178,10 +178,16 @@ def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb):
     r_ids = torch.empty_like(idt)
     r_g = torch.empty_like(gt)
     ms_router = time_loop(torch, lambda i: ops.moe_router(lg, wl.topk, r_ids, r_g), steps, warmup)
+    # the whole block from the same logits in one call (tq4_moe_block)
+    wsb = torch.zeros(ops.moe_block_workspace_size(wl.t, wl.topk, wl.n_experts, wl.n1, wl.k),
+                      dtype=torch.uint8, device=dev)
+    ms_block = time_loop(torch, lambda i: ops.moe_block(x, lg, wl.topk, experts[0], experts[1], sb,
+                                                        out=out, workspace=wsb), steps, warmup)
     touched = np.unique(ids).size
     per_expert = (wl.n1 * (wl.k // 32) + wl.k * (wl.n1 // 32)) * 20
     pairs = wl.t * wl.topk
-    return dict(ms_step=ms, ms_router=ms_router, packed_bytes=touched * per_expert,
+    return dict(ms_step=ms, ms_router=ms_router, ms_block=ms_block,
+                packed_bytes=touched * per_expert,
                 flops=2.0 * pairs * 2 * wl.n1 * wl.k, experts_touched=int(touched))
 
 
@@ -487,6 +493,7 @@ def main() -> int:
             legs[name] = {"ms_per_step": round(q["ms_step"], 4), "GB/s": round(g2, 1),
                           "TFLOP/s": round(tf, 2), "experts_touched": q["experts_touched"],
                           "router_us": round(q["ms_router"] * 1e3, 2),
+                          "block_from_logits_us": round(q["ms_block"] * 1e3, 2),
                           "roofline": {"bound": "hbm", "achieved": round(g2, 1),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": round(g2 / HBM_PEAK_GBS, 4)}}

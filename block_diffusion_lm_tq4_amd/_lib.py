@@ -48,6 +48,9 @@ SIGNATURES = {
     "tq4_linear_fp8_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "tq4_linear_fp8": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "tq4_linear_fp8_quantized": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "tq4_moe_block_workspace_size": (ctypes.c_size_t, [_I64, _I32, _I32, _I64, _I64]),
+    "tq4_moe_block": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _I32, _P, _I64, _P, _U32, _P, _P,
+                                     _SZ, _P]),
     "tq4_linear_rotated": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "tq4_moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
     "tq4_moe_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64]),

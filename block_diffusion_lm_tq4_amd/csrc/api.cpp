@@ -255,25 +255,16 @@ size_t tq4_moe_workspace_size(int64_t t, int32_t topk, int32_t n_experts, int64_
   return moe_layout(t, topk, n_experts, n1, k, p).total;
 }
 
-int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t *topk_ids,
-                    const float *topk_w, int32_t topk, int32_t n_experts,
-                    const uint8_t *w1_packed, int64_t n1, const uint8_t *w2_packed,
-                    uint32_t sign_bits, float *out, void *workspace, size_t workspace_bytes,
-                    void *stream) {
-  if (!moe_shape_ok(t, topk, n_experts, n1, k)) return TQ4_E_SHAPE;
-  if (t == 0) return TQ4_OK;
-  if (x_bf16 == nullptr || topk_ids == nullptr || topk_w == nullptr || w1_packed == nullptr ||
-      w2_packed == nullptr || out == nullptr)
-    return TQ4_E_NULL;
-  if (!aligned(x_bf16, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
-      !aligned(w1_packed, 4) || !aligned(w2_packed, 4) || !aligned(out, 16))
-    return TQ4_E_ALIGN;
+namespace {
+
+// The layer after validation: workspace of at least moe_layout(...).total
+// bytes, 256-byte aligned.
+hipError_t moe_layer(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t *topk_ids,
+                     const float *topk_w, int32_t topk, int32_t n_experts,
+                     const uint8_t *w1_packed, int64_t n1, const uint8_t *w2_packed,
+                     uint32_t sign_bits, float *out, char *ws, hipStream_t s) {
   const MoEPlan p = tq4::plan_moe(t * topk, n_experts);
   const MoELayout l = moe_layout(t, topk, n_experts, n1, k, p);
-  if (workspace == nullptr || workspace_bytes < l.total) return TQ4_E_WORKSPACE;
-  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
-
-  char *ws = static_cast<char *>(workspace);
   int32_t *counts = reinterpret_cast<int32_t *>(ws + l.counts);
   int32_t *offsets = reinterpret_cast<int32_t *>(ws + l.offsets);
   int32_t *perm = reinterpret_cast<int32_t *>(ws + l.perm);
@@ -284,8 +275,6 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t 
   uint16_t *ht = reinterpret_cast<uint16_t *>(ws + l.ht);
   float *o = reinterpret_cast<float *>(ws + l.o);
   const int64_t pairs = t * topk;
-  hipStream_t s = as_stream(stream);
-
   hipError_t e = tq4::launch_route(topk_ids, pairs, topk, n_experts, counts, offsets, perm, inv,
                                    tiles, meta, p.tile_rows, nullptr, s, x_bf16, t * (k / 32),
                                    sign_bits, xt);
@@ -296,6 +285,73 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t 
     e = tq4::launch_moe_gemm(p, 1, ht, n1, perm, topk, w2_packed, k, tiles, meta, o, nullptr,
                              sign_bits, s);
   if (e == hipSuccess) e = tq4::launch_combine(o, inv, topk_w, t, topk, k, out, s);
+  return e;
+}
+
+int moe_args_status(const uint16_t *x_bf16, const uint8_t *w1_packed, const uint8_t *w2_packed,
+                     const float *out) {
+  if (x_bf16 == nullptr || w1_packed == nullptr || w2_packed == nullptr || out == nullptr)
+    return TQ4_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(w1_packed, 4) || !aligned(w2_packed, 4) ||
+      !aligned(out, 16))
+    return TQ4_E_ALIGN;
+  return TQ4_OK;
+}
+
+}  // namespace
+
+int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t *topk_ids,
+                    const float *topk_w, int32_t topk, int32_t n_experts,
+                    const uint8_t *w1_packed, int64_t n1, const uint8_t *w2_packed,
+                    uint32_t sign_bits, float *out, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  if (!moe_shape_ok(t, topk, n_experts, n1, k)) return TQ4_E_SHAPE;
+  if (t == 0) return TQ4_OK;
+  if (topk_ids == nullptr || topk_w == nullptr) return TQ4_E_NULL;
+  const int st = moe_args_status(x_bf16, w1_packed, w2_packed, out);
+  if (st != TQ4_OK) return st;
+  if (!aligned(topk_ids, 4) || !aligned(topk_w, 4)) return TQ4_E_ALIGN;
+  const MoEPlan p = tq4::plan_moe(t * topk, n_experts);
+  const MoELayout l = moe_layout(t, topk, n_experts, n1, k, p);
+  if (workspace == nullptr || workspace_bytes < l.total) return TQ4_E_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
+  return device_status(moe_layer(x_bf16, t, k, topk_ids, topk_w, topk, n_experts, w1_packed, n1,
+                                 w2_packed, sign_bits, out, static_cast<char *>(workspace),
+                                 as_stream(stream)));
+}
+
+size_t tq4_moe_block_workspace_size(int64_t t, int32_t topk, int32_t n_experts, int64_t n1,
+                                    int64_t k) {
+  if (!moe_shape_ok(t, topk, n_experts, n1, k)) return 0;
+  const size_t layer = tq4_moe_workspace_size(t, topk, n_experts, n1, k);
+  if (layer == 0) return 0;
+  const size_t slots = static_cast<size_t>(t) * static_cast<size_t>(topk);
+  return layer + align_up(slots * sizeof(int32_t)) + align_up(slots * sizeof(float));
+}
+
+int tq4_moe_block(const uint16_t *x_bf16, int64_t t, int64_t k, const float *logits,
+                  int32_t n_experts, int32_t topk, const uint8_t *w1_packed, int64_t n1,
+                  const uint8_t *w2_packed, uint32_t sign_bits, float *out, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  if (!moe_shape_ok(t, topk, n_experts, n1, k)) return TQ4_E_SHAPE;
+  if (t == 0) return TQ4_OK;
+  if (logits == nullptr) return TQ4_E_NULL;
+  const int st = moe_args_status(x_bf16, w1_packed, w2_packed, out);
+  if (st != TQ4_OK) return st;
+  if (!aligned(logits, 4)) return TQ4_E_ALIGN;
+  const size_t need = tq4_moe_block_workspace_size(t, topk, n_experts, n1, k);
+  if (workspace == nullptr || workspace_bytes < need) return TQ4_E_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
+  char *ws = static_cast<char *>(workspace);
+  const size_t layer = tq4_moe_workspace_size(t, topk, n_experts, n1, k);
+  const size_t slots = static_cast<size_t>(t) * static_cast<size_t>(topk);
+  int32_t *ids = reinterpret_cast<int32_t *>(ws + layer);
+  float *gates = reinterpret_cast<float *>(ws + layer + align_up(slots * sizeof(int32_t)));
+  hipStream_t s = as_stream(stream);
+  hipError_t e = tq4::launch_router(logits, t, n_experts, topk, ids, gates, s);
+  if (e == hipSuccess)
+    e = moe_layer(x_bf16, t, k, ids, gates, topk, n_experts, w1_packed, n1, w2_packed, sign_bits,
+                  out, ws, s);
   return device_status(e);
 }
 

@@ -296,6 +296,25 @@ int tq4_moe_grouped(const uint16_t *x_bf16, int64_t t, int64_t k,
 int tq4_moe_router(const float *logits, int64_t t, int32_t n_experts, int32_t topk,
                    int32_t *topk_ids, float *topk_w, void *stream);
 
+/* Workspace bytes tq4_moe_block needs (0 if the sizes are invalid). */
+size_t tq4_moe_block_workspace_size(int64_t t, int32_t topk, int32_t n_experts,
+                                    int64_t n1, int64_t k);
+
+/* The whole MoE block of a denoiser step, from router logits to the layer's
+ * output, on one stream and without the host (model card, Running it:
+ * "sync-free MoE"; The model underneath: 128 experts, top-6):
+ * tq4_moe_router into the workspace, then tq4_moe_grouped with those ids and
+ * gates.  Graph-capturable like every call here.  Results equal those of
+ * the two calls made separately, bit for bit.
+ *   logits : [t, n_experts] fp32, device, 4-byte aligned, finite
+ *   other arguments as tq4_moe_grouped; workspace of at least
+ *   tq4_moe_block_workspace_size(...) bytes, 256-byte aligned.
+ * Errors as tq4_moe_grouped. */
+int tq4_moe_block(const uint16_t *x_bf16, int64_t t, int64_t k, const float *logits,
+                  int32_t n_experts, int32_t topk, const uint8_t *w1_packed, int64_t n1,
+                  const uint8_t *w2_packed, uint32_t sign_bits, float *out, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
 /* Measurement aid, not a step of the method: reads `bytes` bytes of device
  * memory at `src` once (16 bytes per thread, one launch) and discards them.
  * Timing one call over the footprint of a packed matrix gives the read

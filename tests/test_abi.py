@@ -210,6 +210,29 @@ def test_fp8_argument_errors(L):
     assert q(FAKE, FAKE, 100, 2690, FAKE, 8192, FAKE, None) == E_SHAPE
 
 
+def test_moe_block_argument_errors(L):
+    ws = L.tq4_moe_block_workspace_size(16, 6, 128, 1856, 2688)
+    assert ws > L.tq4_moe_workspace_size(16, 6, 128, 1856, 2688)
+    assert L.tq4_moe_block_workspace_size(16, 6, 128, 1850, 2688) == 0
+
+    def call(**kw):
+        a = dict(dict(x=FAKE, t=16, k=2688, lg=FAKE, e=128, topk=6, w1=FAKE, n1=1856, w2=FAKE,
+                      out=FAKE, ws=FAKE, wsb=ws), **kw)
+        return L.tq4_moe_block(a["x"], a["t"], a["k"], a["lg"], a["e"], a["topk"], a["w1"],
+                               a["n1"], a["w2"], 0, a["out"], a["ws"], a["wsb"], None)
+
+    assert call(topk=129) == E_SHAPE
+    assert call(e=513) == E_SHAPE
+    assert call(n1=1850) == E_SHAPE
+    assert call(lg=None) == E_NULL
+    assert call(w1=None) == E_NULL
+    assert call(lg=FAKE + 2) == E_ALIGN
+    assert call(x=MIS) == E_ALIGN
+    assert call(ws=None) == E_WS
+    assert call(wsb=ws - 1) == E_WS
+    assert call(t=0) == OK
+
+
 def test_moe_argument_errors(L):
     ws = L.tq4_moe_workspace_size(16, 6, 128, 1856, 2688)
     assert ws > 0

@@ -517,6 +517,28 @@ def test_moe_from_logits_matches_oracle(dev, experts):
     _check_close(out.cpu().numpy(), ref, "moe from logits")
 
 
+@pytest.mark.parametrize("name", ["moe_t16", "moe_t1024_zipf"])
+def test_moe_block_matches_oracle_and_the_two_calls(dev, experts, name):
+    # tq4_moe_block: router + layer in one call; the same bits as the two
+    # calls made separately, and the oracle's router + layer on sampled tokens
+    wl = I.WORKLOADS[name]
+    routing = "zipf" if "zipf" in name else "uniform"
+    lg = I.router_logits(wl.t, wl.n_experts, routing, seed=7).astype(np.float32)
+    x_bits = I.activations_bf16(wl.t, wl.k, seed=8)
+    xb = _bf16(x_bits, dev)
+    lg_d = torch.from_numpy(lg).to(dev)
+    out = _ops().moe_block(xb, lg_d, wl.topk, experts[0], experts[1], SB)
+    ids, g = _ops().moe_router(lg_d, wl.topk)
+    two = _ops().moe_grouped(xb, ids, g, experts[0], experts[1], SB)
+    torch.cuda.synchronize()
+    assert torch.equal(out, two)
+    tokens = np.arange(wl.t) if wl.t <= 16 else np.unique(np.r_[np.arange(0, wl.t, 97), wl.t - 1])
+    ref_ids, ref_g = O.router(lg[tokens], wl.topk)
+    ref = O.moe(x_bits[tokens], ref_ids, ref_g, _oracle_expert(experts, 1),
+                _oracle_expert(experts, 2), SB)
+    _check_close(out.cpu().numpy()[tokens], ref, f"moe block {name}")
+
+
 def test_moe_deterministic(dev, experts):
     wl = I.WORKLOADS["moe_t1024_zipf"]
     ids, g = I.moe_routing(wl)
