@@ -195,9 +195,11 @@ size_t tq4_fp8_cache_size(int64_t n, int64_t k);
  * encoded as above.  cache: device, 16-byte aligned, tq4_fp8_cache_size
  * bytes.  The codes are exactly those of the rule above whenever the two
  * half-block scales of each block are within a factor 2^12 of each other
- * (then every sum of the inverse rotation is exact in fp64).  Offline, like
- * tq4_pack.  Errors: TQ4_E_NULL, TQ4_E_SHAPE (negative sizes, k % 32 != 0,
- * kp >= 2^23), TQ4_E_ALIGN, TQ4_E_DEVICE.  n == 0 or k == 0 is a no-op. */
+ * (then every sum of the inverse rotation is exact in fp64).  A block whose
+ * decoded values are not finite (a NaN or infinite scale) gets unspecified
+ * codes.  Offline, like tq4_pack.  Errors: TQ4_E_NULL, TQ4_E_SHAPE (negative
+ * sizes, k % 32 != 0, kp >= 2^23), TQ4_E_ALIGN, TQ4_E_DEVICE.  n == 0 or
+ * k == 0 is a no-op. */
 int tq4_fp8_cache(const uint8_t *packed, int64_t n, int64_t k, uint32_t sign_bits,
                   uint8_t *cache, void *stream);
 
