@@ -188,7 +188,10 @@ struct WRaw {
 
 // LUTC copies of the pair table are interleaved (entry e of copy q at
 // e * LUTC + q; lane L uses copy L % LUTC), so that random lookups by the
-// lanes of a wave spread over the LDS banks.
+// lanes of a wave spread over the LDS banks.  The small-tile configurations
+// use one copy: the lookup address is then the code byte times 4, one
+// byte-select shift per lookup (SDWA) instead of an extract and a shift-or,
+// and on this table a single copy measured no slower than eight.
 // Occupancy targets (waves per SIMD) for the tile heights the MoE layer
 // uses: more resident workgroups hide the per-chunk load latency better than
 // the registers the compiler would otherwise spend (measured on the MoE
@@ -899,10 +902,10 @@ hipError_t dispatch(int msub, int nsub, int waves_m, const GemmArgs &g, dim3 gri
                     hipStream_t s) {
   if (nsub == 2 && waves_m == 1) {
     switch (msub) {
-      case 1: return launch_cfg<1, 2, 8, MODE>(g, grid, s);
-      case 2: return launch_cfg<2, 2, 8, MODE>(g, grid, s);
-      case 3: return launch_cfg<3, 2, 8, MODE>(g, grid, s);
-      case 4: return launch_cfg<4, 2, 8, MODE>(g, grid, s);
+      case 1: return launch_cfg<1, 2, 1, MODE>(g, grid, s);
+      case 2: return launch_cfg<2, 2, 1, MODE>(g, grid, s);
+      case 3: return launch_cfg<3, 2, 1, MODE>(g, grid, s);
+      case 4: return launch_cfg<4, 2, 1, MODE>(g, grid, s);
       default: break;
     }
   }

@@ -308,7 +308,10 @@ constexpr int kChunkBytes = kRowsPerWG * kChunkRowBytes;    // 2560
 constexpr int kSlotBytes = kXSliceBytes + kChunkBytes;      // 6656
 constexpr int kDmaMaxK = 2944;
 constexpr int kDmaMaxChunks = kDmaMaxK / 128;               // 23
-constexpr int kDmaLutCopies = 8;
+// One pair table: a lookup address is then the code byte times 4 (one
+// byte-select shift), and a single copy measured faster here than eight
+// interleaved ones (7.4 against 7.6 us per call).
+constexpr int kDmaLutCopies = 1;
 
 typedef __attribute__((address_space(3))) volatile uint32_t lds_flag;
 
