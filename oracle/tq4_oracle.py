@@ -343,7 +343,7 @@ def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
         rows, js = np.nonzero(sel == e)
         h = np.maximum(x[t_all[rows]] @ w1.T, 0.0) ** 2
         o = h @ w2.T
-        out[rows] += g[t_all[rows], js][:, None] * o
+        np.add.at(out, rows, g[t_all[rows], js][:, None] * o)  # a token may list e twice
     return out
 
 

@@ -148,6 +148,12 @@ def test_moe_special_cases():
     g2[:, 0] = 0
     assert np.allclose(O.moe(x, bad, g, w1, w2, SB), O.moe(x, ids, g2, w1, w2, SB),
                        rtol=1e-13, atol=1e-15)
+    # a token that lists one expert in two slots gets both terms: the same as
+    # one slot whose gate is the sum of the two
+    dup = np.stack([ids[:, 0], ids[:, 0]], axis=1)
+    gd = g[:, :2].astype(np.float64)
+    one = O.moe(x, ids[:, :1], (gd[:, 0] + gd[:, 1])[:, None], w1, w2, SB)
+    assert np.allclose(O.moe(x, dup, gd, w1, w2, SB), one, rtol=1e-13, atol=1e-15)
 
 
 def test_bucketing_invariants_and_brute_force():
