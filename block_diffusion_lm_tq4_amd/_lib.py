@@ -56,6 +56,9 @@ SIGNATURES = {
     "tq4_moe_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64]),
     "tq4_moe_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _P, _I64, _P, _U32,
                                        _P, _P, _SZ, _P]),
+    "tq4_moe_grouped_fp8_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64]),
+    "tq4_moe_grouped_fp8": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _P, _I64, _P,
+                                           _P, _P, _SZ, _P]),
     "tq4_moe_router": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "tq4_read_probe": (ctypes.c_int, [_P, _I64, _P, _P]),
 }

@@ -442,6 +442,105 @@ int tq4_linear_fp8_quantized(const uint8_t *x_codes, const uint8_t *x_scales, in
       tq4::launch_linear_fp8(x_codes, x_scales, m, k, cache, cache + n * kp, n, y, s));
 }
 
+// ---- fp8 MoE --------------------------------------------------------------
+
+namespace {
+
+struct MoEFp8Layout {
+  int tile_rows;
+  int64_t max_tiles;
+  size_t counts, offsets, perm, inv, tiles, meta, xq, xs, hq, hs, o, total;
+};
+
+MoEFp8Layout moe_fp8_layout(int64_t t, int32_t topk, int32_t e, int64_t n1, int64_t k) {
+  const int64_t pairs = t * topk;
+  const int64_t kp = tq4::fp8_padded_k(k);
+  const int64_t n1p = tq4::fp8_padded_k(n1);
+  MoEFp8Layout l{};
+  l.tile_rows = tq4::fp8_moe_tile_rows(pairs, e);
+  const int64_t busy = pairs < e ? pairs : e;
+  l.max_tiles = pairs / l.tile_rows + busy + 1;
+  const size_t p = static_cast<size_t>(pairs);
+  size_t off = 0;
+  l.counts = off;  off += align_up(sizeof(int32_t) * e);
+  l.offsets = off; off += align_up(sizeof(int32_t) * (e + 1));
+  l.perm = off;    off += align_up(sizeof(int32_t) * p);
+  l.inv = off;     off += align_up(sizeof(int32_t) * p);
+  l.tiles = off;   off += align_up(sizeof(MoETile) * static_cast<size_t>(l.max_tiles));
+  l.meta = off;    off += kAlign;
+  l.xq = off;      off += align_up(static_cast<size_t>(t) * kp);
+  l.xs = off;      off += align_up(static_cast<size_t>(t) * (kp / 32));
+  l.hq = off;      off += align_up(p * n1p);
+  l.hs = off;      off += align_up(p * (n1p / 32));
+  l.o = off;       off += align_up(p * k * 4);
+  l.total = off;
+  return l;
+}
+
+bool moe_fp8_shape_ok(int64_t t, int32_t topk, int32_t e, int64_t n1, int64_t k) {
+  if (!moe_shape_ok(t, topk, e, n1, k)) return false;
+  if (!tq4::fp8_shape_fits(1, k, 1) || !tq4::fp8_shape_fits(1, n1, 1)) return false;
+  if (!tq4::fp8_moe_shape_fits(t, k, n1) || !tq4::fp8_moe_shape_fits(t * topk, n1, k))
+    return false;
+  return moe_fp8_layout(t, topk, e, n1, k).max_tiles <= 65535;
+}
+
+}  // namespace
+
+size_t tq4_moe_grouped_fp8_workspace_size(int64_t t, int32_t topk, int32_t n_experts, int64_t n1,
+                                          int64_t k) {
+  if (!moe_fp8_shape_ok(t, topk, n_experts, n1, k)) return 0;
+  return moe_fp8_layout(t, topk, n_experts, n1, k).total;
+}
+
+int tq4_moe_grouped_fp8(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t *topk_ids,
+                        const float *topk_w, int32_t topk, int32_t n_experts,
+                        const uint8_t *w1_cache, int64_t n1, const uint8_t *w2_cache, float *out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  if (!moe_fp8_shape_ok(t, topk, n_experts, n1, k)) return TQ4_E_SHAPE;
+  if (t == 0) return TQ4_OK;
+  if (x_bf16 == nullptr || topk_ids == nullptr || topk_w == nullptr || w1_cache == nullptr ||
+      w2_cache == nullptr || out == nullptr)
+    return TQ4_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      !aligned(w1_cache, 16) || !aligned(w2_cache, 16) || !aligned(out, 16))
+    return TQ4_E_ALIGN;
+  const MoEFp8Layout l = moe_fp8_layout(t, topk, n_experts, n1, k);
+  if (workspace == nullptr || workspace_bytes < l.total) return TQ4_E_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
+  char *ws = static_cast<char *>(workspace);
+  int32_t *counts = reinterpret_cast<int32_t *>(ws + l.counts);
+  int32_t *offsets = reinterpret_cast<int32_t *>(ws + l.offsets);
+  int32_t *perm = reinterpret_cast<int32_t *>(ws + l.perm);
+  int32_t *inv = reinterpret_cast<int32_t *>(ws + l.inv);
+  MoETile *tiles = reinterpret_cast<MoETile *>(ws + l.tiles);
+  int32_t *meta = reinterpret_cast<int32_t *>(ws + l.meta);
+  uint8_t *xq = reinterpret_cast<uint8_t *>(ws + l.xq);
+  uint8_t *xs = reinterpret_cast<uint8_t *>(ws + l.xs);
+  uint8_t *hq = reinterpret_cast<uint8_t *>(ws + l.hq);
+  uint8_t *hs = reinterpret_cast<uint8_t *>(ws + l.hs);
+  float *o = reinterpret_cast<float *>(ws + l.o);
+  const int64_t pairs = t * topk;
+  const int64_t kp = tq4::fp8_padded_k(k);
+  const int64_t n1p = tq4::fp8_padded_k(n1);
+  // stacked caches: codes of all E * rows rows, then their scale bytes
+  const uint8_t *w1s = w1_cache + static_cast<int64_t>(n_experts) * n1 * kp;
+  const uint8_t *w2s = w2_cache + static_cast<int64_t>(n_experts) * k * n1p;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = tq4::launch_act_mxfp8(x_bf16, t, k, xq, xs, s);
+  if (e == hipSuccess)
+    e = tq4::launch_route(topk_ids, pairs, topk, n_experts, counts, offsets, perm, inv, tiles,
+                          meta, l.tile_rows, nullptr, s);
+  if (e == hipSuccess)
+    e = tq4::launch_moe_fp8(0, l.tile_rows, xq, xs, t, k, perm, topk, w1_cache, w1s, n1, n1p,
+                            tiles, meta, l.max_tiles, nullptr, hq, hs, s);
+  if (e == hipSuccess)
+    e = tq4::launch_moe_fp8(1, l.tile_rows, hq, hs, pairs, n1, perm, topk, w2_cache, w2s, k, k,
+                            tiles, meta, l.max_tiles, o, nullptr, nullptr, s);
+  if (e == hipSuccess) e = tq4::launch_combine(o, inv, topk_w, t, topk, k, out, s);
+  return device_status(e);
+}
+
 int tq4_read_probe(const void *src, int64_t bytes, float *sink, void *stream) {
   if (bytes < 0 || bytes % 16 != 0) return TQ4_E_SHAPE;
   if (bytes == 0) return TQ4_OK;

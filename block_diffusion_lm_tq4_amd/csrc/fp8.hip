@@ -139,11 +139,43 @@ __global__ __launch_bounds__(256) void fp8_cache_kernel(const uint8_t *__restric
   scales[t] = static_cast<uint8_t>(e + 127);
 }
 
-// One thread per 32-element activation block: bf16 -> fp32 (exact), block
-// exponent, codes of x / 2^e (exact scaling, then one hardware rounding to
-// nearest even).
-__global__ __launch_bounds__(256) void act_mxfp8_kernel(const uint16_t *__restrict__ x,
-                                                        int64_t m, int32_t kb, int32_t kpb,
+// One thread per 32-element activation block: bf16 -> fp32 (exact) or fp32
+// as is, block exponent, codes of x / 2^e (exact scaling, then one hardware
+// rounding to nearest even).
+template <typename In>
+__device__ inline void load_block32(const In *src, float (&v)[32]);
+
+template <>
+__device__ inline void load_block32<uint16_t>(const uint16_t *src, float (&v)[32]) {
+  const uint4 *q = reinterpret_cast<const uint4 *>(src);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 d = q[i];
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <>
+__device__ inline void load_block32<float>(const float *src, float (&v)[32]) {
+  const float4 *q = reinterpret_cast<const float4 *>(src);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 d = q[i];
+    v[4 * i] = d.x;
+    v[4 * i + 1] = d.y;
+    v[4 * i + 2] = d.z;
+    v[4 * i + 3] = d.w;
+  }
+}
+
+template <typename In>
+__global__ __launch_bounds__(256) void act_mxfp8_kernel(const In *__restrict__ x, int64_t m,
+                                                        int32_t kb, int32_t kpb,
                                                         uint8_t *__restrict__ codes,
                                                         uint8_t *__restrict__ scales) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -157,18 +189,8 @@ __global__ __launch_bounds__(256) void act_mxfp8_kernel(const uint16_t *__restri
     scales[t] = 0;
     return;
   }
-  const uint4 *src = reinterpret_cast<const uint4 *>(x + (row * kb + col) * 32);
   float v[32];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 d = src[i];
-    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-  }
+  load_block32<In>(x + (row * kb + col) * 32, v);
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
@@ -603,6 +625,250 @@ __global__ __launch_bounds__(64 * kF8Waves) void fp8_gemm_kernel(F8Args g) {
     }
 }
 
+// Grouped MoE product over the fp8 expert caches.  One workgroup of 8 waves
+// per (MoE tile, 256 output columns): the tile's activation rows (16 * MT of
+// them, gathered through the bucket permutation for the up projection) and
+// the expert's 256 weight rows stream through S LDS stages of one 128-k step
+// each, S - 1 steps ahead, as in fp8_gemm_kernel (same XOR swizzle, same
+// exact load-count waits).  Wave w owns output columns 32 w .. 32 w + 31 of
+// the slab: two 16-column tiles against all MT row tiles.
+//   up (MODE 0):   h = relu(acc)^2 in fp32, then MXFP8 of h per row and
+//                  32-block -- a wave's 32 columns are exactly one block --
+//                  stored as codes hq[row][np] and scale bytes hs[row][np/32]
+//                  (np = hidden width padded to 128: the padding blocks have
+//                  zero weights, so they come out as zero codes and scale 0).
+//   down (MODE 1): out[row][n] = acc (fp32), rows in bucket order.
+// Rows past the tile's end load the tile's first row (not stored); weight
+// rows past n read zeros through the buffer range.
+constexpr int kF8MoeWaves = 8;
+constexpr int kF8MoeTN = 32 * kF8MoeWaves;  // 256 output columns per workgroup
+
+struct F8MoeArgs {
+  const uint8_t *aq;  // activation codes: up [t][kp] (gathered), down [pairs][kp]
+  const uint8_t *as;  // their scale bytes [.][kpb]
+  const uint8_t *wq;  // expert codes [E * n][kp]
+  const uint8_t *ws;  // expert scale bytes [E * n][kpb]
+  const int32_t *perm;
+  const MoETile *tiles;
+  const int32_t *n_tiles;
+  float *out;         // down: [pairs][n]
+  uint8_t *hq;        // up: [pairs][n_store]
+  uint8_t *hs;        // up: [pairs][n_store / 32]
+  int64_t n;          // weight rows per expert
+  int64_t n_store;    // up: hidden width padded to 128; down: n
+  int64_t a_rows;     // rows of aq
+  int32_t kp, kpb, chunks, topk;
+};
+
+template <int MT>
+constexpr int f8_moe_stages() {
+  return MT == 1 ? 4 : 3;
+}
+
+template <int MT, int MODE>
+__global__ __launch_bounds__(64 * kF8MoeWaves) void fp8_moe_kernel(F8MoeArgs g) {
+  constexpr int TM = 16 * MT;
+  constexpr int S = f8_moe_stages<MT>();
+  constexpr int kA = TM * kF8Row;                 // activation rows of a stage
+  constexpr int kB = kF8MoeTN * kF8Row;           // weight rows of a stage
+  constexpr int kStage = kA + kB + 512 * 4;       // then 512 scale words
+  constexpr int kSc = kA + kB;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S * kStage];
+
+  if (static_cast<int32_t>(blockIdx.y) >= *g.n_tiles) return;
+  const MoETile tile = g.tiles[blockIdx.y];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int r = lane % 16;
+  const int grp = lane / 16;
+  const int kp = g.kp;
+  const int kpb = g.kpb;
+  const int rows = tile.rows;
+  const int64_t m_base = tile.row0;
+  const int64_t n_base = static_cast<int64_t>(blockIdx.x) * kF8MoeTN;
+  const int64_t w_valid = g.n - n_base < kF8MoeTN ? (g.n - n_base > 0 ? g.n - n_base : 0)
+                                                  : kF8MoeTN;
+
+  // source row of local activation row i (rows past the tile's end: row 0)
+  auto src_row = [&](int i) __attribute__((always_inline)) -> int64_t {
+    const int64_t local = i < rows ? i : 0;
+    if constexpr (MODE == 0) return g.perm[m_base + local] / g.topk;
+    return m_base + local;
+  };
+
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.aq), static_cast<short>(0), static_cast<int>(g.a_rows * kp),
+      kF8BufferFlags);
+  const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.as), static_cast<short>(0), static_cast<int>(g.a_rows * kpb),
+      kF8BufferFlags);
+  const int64_t w_row0 = static_cast<int64_t>(tile.expert) * g.n + n_base;
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.wq + w_row0 * kp), static_cast<short>(0),
+      static_cast<int>(w_valid * kp), kF8BufferFlags);
+  const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(g.ws + w_row0 * kpb), static_cast<short>(0),
+      static_cast<int>(w_valid * kpb), kF8BufferFlags);
+
+  // Activation loads.  MT == 1: 16 rows x 128 bytes = one dword per lane of
+  // the workgroup; lane l of wave w fills LDS bytes 256 w + 4 l, i.e. row
+  // 2 w + l / 32, stored slot (l % 32) / 4, dword l % 4, whose key
+  // (row / 2) % 8 is w.  MT >= 4: 1 KB pieces of 8 rows, MT / 4 per wave;
+  // lane l fills row 8 p + l / 8 at stored slot l % 8.
+  constexpr int kAPieces = MT == 1 ? 1 : MT / 4;
+  static_assert(kAPieces <= 2, "at most two activation pieces per wave");
+  // (a bound that depends on MT here made the host pass drop launch stubs)
+  uint32_t a_voff[2];
+  if constexpr (MT == 1) {
+    const int row = 2 * wave + lane / 32;
+    a_voff[0] = static_cast<uint32_t>(src_row(row) * kp + 16 * (((lane % 32) / 4) ^ wave) +
+                                      4 * (lane % 4));
+  } else {
+#pragma unroll
+    for (int i = 0; i < kAPieces; ++i) {
+      const int piece = kAPieces * wave + i;
+      const int row = 8 * piece + lane / 8;
+      a_voff[i] = static_cast<uint32_t>(src_row(row) * kp + 16 * ((lane % 8) ^ ((row >> 1) % 8)));
+    }
+  }
+  // Weight loads: wave w takes pieces 4 w .. 4 w + 3, i.e. exactly the rows of
+  // its own 32 columns; the key of piece p is (l / 16) ^ 4 (p % 2).
+  const int key0 = (lane % 8) ^ (lane / 16);
+  const uint32_t w_voff_even = static_cast<uint32_t>((lane / 8) * kp + 16 * key0);
+  const uint32_t w_voff_odd = static_cast<uint32_t>((lane / 8) * kp + 16 * (key0 ^ 4));
+  // Scale words (4 bytes per row and step): waves 0-3 load weight rows
+  // 64 w + l into words 64 w + l; waves 4-7 load activation rows
+  // min(64 (w - 4) + l, TM - 1) into words 64 w + l, so activation row i sits
+  // at word 256 + i and the clamped repeats land in words nothing reads.
+  const bool s_w = wave < 4;
+  uint32_t s_voff;
+  if (s_w) {
+    s_voff = static_cast<uint32_t>((64 * wave + lane) * kpb);
+  } else {
+    const int arow = 64 * (wave - 4) + lane < TM ? 64 * (wave - 4) + lane : TM - 1;
+    s_voff = static_cast<uint32_t>(src_row(arow) * kpb);
+  }
+
+  const int chunks = g.chunks;
+  auto issue = [&](int c, uint8_t *st) __attribute__((always_inline)) {
+    const int cc = c < chunks ? c : chunks - 1;  // padding steps reload the last one
+    if constexpr (MT == 1) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void *)(st + 256 * wave), 4,
+                                               a_voff[0], kF8Row * cc, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kAPieces; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            a_rsrc, (lds_void *)(st + (kAPieces * wave + i) * 1024), 16, a_voff[i],
+            kF8Row * cc, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int piece = 4 * wave + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rsrc, (lds_void *)(st + kA + piece * 1024), 16, i % 2 ? w_voff_odd : w_voff_even,
+          8 * piece * kp + kF8Row * cc, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_w ? ws_rsrc : as_rsrc,
+                                             (lds_void *)(st + kSc + 256 * wave), 4, s_voff,
+                                             4 * cc, 0, 0);
+  };
+
+  floatx4 acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint8_t *st) __attribute__((always_inline)) {
+    intx8 bq[2];
+    int sb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 32 * wave + 16 * j + r;
+      const int key = (row >> 1) % 8;
+      const uint8_t *base = st + kA + row * kF8Row;
+      bq[j] = join(*reinterpret_cast<const uint4 *>(base + 16 * (grp ^ key)),
+                   *reinterpret_cast<const uint4 *>(base + 16 * ((4 + grp) ^ key)));
+      sb[j] = st[kSc + 4 * row + grp];
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int row = 16 * i + r;
+      const int key = (row >> 1) % 8;
+      const uint8_t *base = st + row * kF8Row;
+      const intx8 aq = join(*reinterpret_cast<const uint4 *>(base + 16 * (grp ^ key)),
+                            *reinterpret_cast<const uint4 *>(base + 16 * ((4 + grp) ^ key)));
+      const int sa = st[kSc + 4 * (256 + row) + grp];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq, bq[j], acc[i][j], 0, 0,
+                                                                     0, sa, 0, sb[j]);
+    }
+  };
+
+  // Step c: wait until only steps c + 1 .. c + S - 2 are outstanding, barrier
+  // (step c is in LDS for every wave; every wave is done with step c - 1's
+  // stage), refill that stage with step c + S - 1, multiply step c.
+  constexpr int kLoads = kAPieces + 4 + 1;
+  constexpr int kAhead = (S - 2) * kLoads;
+  constexpr int kWait = 0x0F70 | (kAhead & 15) | ((kAhead >> 4) << 14);
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s, smem + s * kStage);
+  for (int c = 0; c < chunks; c += S) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      __builtin_amdgcn_s_waitcnt(kWait);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      issue(c + s + S - 1, smem + ((s + S - 1) % S) * kStage);
+      if (c + s < chunks) compute(smem + s * kStage);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding steps' loads
+
+  const int64_t col0 = n_base + 32 * wave;
+  if constexpr (MODE == 0) {
+    const bool col_ok = col0 < g.n_store;
+    const int64_t npb = g.n_store / 32;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float u0 = acc[i][0][v];
+        const float u1 = acc[i][1][v];
+        const float h0 = u0 > 0.f ? u0 * u0 : 0.f;
+        const float h1 = u1 > 0.f ? u1 * u1 : 0.f;
+        float amax = __builtin_fmaxf(h0, h1);
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, d));
+        const int e = block_exponent_f32(amax);
+        const int pair = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(h0, -e),
+                                                         __builtin_ldexpf(h1, -e), 0, false);
+        const int local = 16 * i + 4 * grp + v;
+        if (col_ok && local < rows) {
+          uint8_t *dst = g.hq + (m_base + local) * g.n_store + col0;
+          dst[r] = static_cast<uint8_t>(pair & 0xFF);
+          dst[16 + r] = static_cast<uint8_t>((pair >> 8) & 0xFF);
+          if (r == 0) g.hs[(m_base + local) * npb + col0 / 32] = static_cast<uint8_t>(e + 127);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = col0 + 16 * j + r;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int local = 16 * i + 4 * grp + v;
+          if (local < rows && n < g.n) g.out[(m_base + local) * g.n + n] = acc[i][j][v];
+        }
+      }
+  }
+}
+
 }  // namespace
 
 int64_t fp8_padded_k(int64_t k) { return (k + 127) / 128 * 128; }
@@ -623,7 +889,17 @@ hipError_t launch_act_mxfp8(const uint16_t *x, int64_t m, int64_t k, uint8_t *co
   const int32_t kpb = static_cast<int32_t>(fp8_padded_k(k) / 32);
   const int64_t threads = m * kpb;
   if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(act_mxfp8_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)),
+  hipLaunchKernelGGL(act_mxfp8_kernel<uint16_t>, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                     dim3(256), 0, s, x, m, static_cast<int32_t>(k / 32), kpb, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_mxfp8_f32(const float *x, int64_t m, int64_t k, uint8_t *codes,
+                                uint8_t *scales, hipStream_t s) {
+  const int32_t kpb = static_cast<int32_t>(fp8_padded_k(k) / 32);
+  const int64_t threads = m * kpb;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(act_mxfp8_kernel<float>, dim3(static_cast<unsigned>((threads + 255) / 256)),
                      dim3(256), 0, s, x, m, static_cast<int32_t>(k / 32), kpb, codes, scales);
   return hipGetLastError();
 }
@@ -668,6 +944,64 @@ hipError_t launch_linear_fp8(const uint8_t *xq, const uint8_t *xs, int64_t m, in
   g.tiles_n = static_cast<int32_t>((n + kF8TN - 1) / kF8TN);
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(g.tiles_m) * g.tiles_n));
   hipLaunchKernelGGL(fp8_gemm_kernel, grid, dim3(64 * kF8Waves), 0, s, g);
+  return hipGetLastError();
+}
+
+int fp8_moe_tile_rows(int64_t pairs, int32_t n_experts) {
+  // about one row per expert: 16-row tiles; otherwise 128 rows, so that a
+  // popular expert's weights are streamed once per 128 of its rows
+  return pairs <= 16 * static_cast<int64_t>(n_experts) ? 16 : 128;
+}
+
+bool fp8_moe_shape_fits(int64_t a_rows, int64_t k, int64_t n) {
+  const int64_t kp = fp8_padded_k(k);
+  return a_rows * kp < (int64_t{1} << 31) && kF8MoeTN * kp < (int64_t{1} << 31) && n >= 1;
+}
+
+hipError_t launch_moe_fp8(int mode, int tile_rows, const uint8_t *aq, const uint8_t *as,
+                          int64_t a_rows, int64_t k, const int32_t *perm, int32_t topk,
+                          const uint8_t *wq, const uint8_t *ws, int64_t n, int64_t n_store,
+                          const MoETile *tiles, const int32_t *n_tiles, int64_t max_tiles,
+                          float *out, uint8_t *hq, uint8_t *hs, hipStream_t s) {
+  if (!fp8_moe_shape_fits(a_rows, k, n) || max_tiles > 65535) return hipErrorInvalidValue;
+  if (mode == 0 && n_store % 128 != 0) return hipErrorInvalidValue;
+  if (max_tiles == 0) return hipSuccess;
+  F8MoeArgs g{};
+  g.aq = aq;
+  g.as = as;
+  g.wq = wq;
+  g.ws = ws;
+  g.perm = perm;
+  g.tiles = tiles;
+  g.n_tiles = n_tiles;
+  g.out = out;
+  g.hq = hq;
+  g.hs = hs;
+  g.n = n;
+  g.n_store = n_store;
+  g.a_rows = a_rows;
+  g.kp = static_cast<int32_t>(fp8_padded_k(k));
+  g.kpb = g.kp / 32;
+  g.chunks = g.kp / 128;
+  g.topk = topk;
+  const dim3 grid(static_cast<unsigned>((n_store + kF8MoeTN - 1) / kF8MoeTN),
+                  static_cast<unsigned>(max_tiles));
+  const dim3 block(64 * kF8MoeWaves);
+  if (mode == 0) {
+    switch (tile_rows) {
+      case 16: hipLaunchKernelGGL((fp8_moe_kernel<1, 0>), grid, block, 0, s, g); break;
+      case 64: hipLaunchKernelGGL((fp8_moe_kernel<4, 0>), grid, block, 0, s, g); break;
+      case 128: hipLaunchKernelGGL((fp8_moe_kernel<8, 0>), grid, block, 0, s, g); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (tile_rows) {
+      case 16: hipLaunchKernelGGL((fp8_moe_kernel<1, 1>), grid, block, 0, s, g); break;
+      case 64: hipLaunchKernelGGL((fp8_moe_kernel<4, 1>), grid, block, 0, s, g); break;
+      case 128: hipLaunchKernelGGL((fp8_moe_kernel<8, 1>), grid, block, 0, s, g); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   return hipGetLastError();
 }
 

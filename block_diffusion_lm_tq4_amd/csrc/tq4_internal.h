@@ -201,6 +201,23 @@ hipError_t launch_linear_fp8(const uint8_t *xq, const uint8_t *xs, int64_t m, in
                              const uint8_t *wq, const uint8_t *ws, int64_t n, float *y,
                              hipStream_t s);
 
+hipError_t launch_act_mxfp8_f32(const float *x, int64_t m, int64_t k, uint8_t *codes,
+                                uint8_t *scales, hipStream_t s);
+// Grouped MoE products over fp8 expert caches (expert e's rows at e * n of
+// the stacked [E * n, k] cache).  mode 0 (up): activation rows gathered as
+// perm[row] / topk from aq [a_rows][kp]; writes MXFP8 codes and scale bytes of
+// relu(acc)^2 into hq [pairs][n_store], hs [pairs][n_store / 32] (n_store =
+// hidden width padded to 128).  mode 1 (down): activation rows are the bucket
+// rows of aq; out[row][n] = acc (fp32).  tile_rows: 16, 64 or 128 (as given
+// to launch_route).
+int fp8_moe_tile_rows(int64_t pairs, int32_t n_experts);
+bool fp8_moe_shape_fits(int64_t a_rows, int64_t k, int64_t n);
+hipError_t launch_moe_fp8(int mode, int tile_rows, const uint8_t *aq, const uint8_t *as,
+                          int64_t a_rows, int64_t k, const int32_t *perm, int32_t topk,
+                          const uint8_t *wq, const uint8_t *ws, int64_t n, int64_t n_store,
+                          const MoETile *tiles, const int32_t *n_tiles, int64_t max_tiles,
+                          float *out, uint8_t *hq, uint8_t *hs, hipStream_t s);
+
 // Streaming read of `bytes` (a multiple of 16) from a 16-byte aligned buffer.
 hipError_t launch_read_probe(const void *src, int64_t bytes, float *sink, hipStream_t s);
 

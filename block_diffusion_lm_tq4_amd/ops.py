@@ -348,6 +348,49 @@ def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
     return out
 
 
+def fp8_cache_experts(packed: torch.Tensor, sign_bits: int) -> torch.Tensor:
+    """Experts' packed weights [E, n, k/32, 20] -> the fp8 cache of the stacked
+    [E * n, k] matrix (the layout tq4_moe_grouped_fp8 takes)."""
+    _require(packed.dim() == 4, "packed must be [E, n, k/32, 20]")
+    e, n, kb, bb = packed.shape
+    return fp8_cache(packed.view(e * n, kb, bb), sign_bits)
+
+
+def moe_grouped_fp8_workspace_size(t: int, topk: int, n_experts: int, n1: int, k: int) -> int:
+    return int(lib().tq4_moe_grouped_fp8_workspace_size(t, topk, n_experts, n1, k))
+
+
+def moe_grouped_fp8(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                    w1_cache: torch.Tensor, w2_cache: torch.Tensor, n_experts: int, n1: int,
+                    out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The MoE layer on fp8 expert caches (tq4_moe_grouped_fp8); fp32 [t, k]."""
+    _cuda_contig(x, "x", torch.bfloat16)
+    _cuda_contig(topk_ids, "topk_ids", torch.int32)
+    _cuda_contig(topk_w, "topk_w", torch.float32)
+    _cuda_contig(w1_cache, "w1_cache", torch.uint8)
+    _cuda_contig(w2_cache, "w2_cache", torch.uint8)
+    t, k = x.shape
+    _require(topk_ids.dim() == 2 and topk_ids.shape[0] == t, "topk_ids must be [t, topk]")
+    topk = topk_ids.shape[1]
+    _require(tuple(topk_w.shape) == (t, topk), "topk_w must be [t, topk]")
+    _require(w1_cache.numel() >= int(lib().tq4_fp8_cache_size(n_experts * n1, k)),
+             "w1_cache too small for [E * n1, k]")
+    _require(w2_cache.numel() >= int(lib().tq4_fp8_cache_size(n_experts * k, n1)),
+             "w2_cache too small for [E * k, n1]")
+    if out is None:
+        out = torch.empty((t, k), dtype=torch.float32, device=x.device)
+    _cuda_contig(out, "out", torch.float32)
+    need = moe_grouped_fp8_workspace_size(t, topk, n_experts, n1, k)
+    if workspace is None:
+        workspace = _WS.get(x.device, "moe_fp8", need)
+    check("tq4_moe_grouped_fp8", lib().tq4_moe_grouped_fp8(
+        x.data_ptr(), t, k, topk_ids.data_ptr(), topk_w.data_ptr(), topk, n_experts,
+        w1_cache.data_ptr(), n1, w2_cache.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream(x.device)))
+    return out
+
+
 def moe_block_workspace_size(t: int, topk: int, n_experts: int, n1: int, k: int) -> int:
     return int(lib().tq4_moe_block_workspace_size(t, topk, n_experts, n1, k))
 

@@ -237,6 +237,37 @@ int tq4_linear_fp8_quantized(const uint8_t *x_codes, const uint8_t *x_scales, in
                              int64_t k, const uint8_t *cache, int64_t n, float *y,
                              void *stream);
 
+/* Workspace bytes tq4_moe_grouped_fp8 needs (0 if the sizes are invalid). */
+size_t tq4_moe_grouped_fp8_workspace_size(int64_t t, int32_t topk, int32_t n_experts,
+                                          int64_t n1, int64_t k);
+
+/* The MoE layer of tq4_moe_grouped on fp8 expert caches (model card, Help
+ * wanted: the resident fp8 copy; Running it: the sync-free MoE):
+ *   out[t, :] = sum_j topk_w[t, j] * dq(q(h_tj)) . dq(W2c_e)^T,
+ *   h_tj = relu(dq(q(x[t, :])) . dq(W1c_e)^T)^2,  e = topk_ids[t, j],
+ * where q is the MXFP8 quantization of tq4_act_mxfp8 (per row and 32-block)
+ * and dq its value; ids outside [0, n_experts) contribute nothing.
+ *   x_bf16   : [t, k] bf16 bit patterns, device, 16-byte aligned
+ *   topk_ids : [t, topk] int32, device;  topk_w : [t, topk] fp32, device
+ *   w1_cache : tq4_fp8_cache of the experts' up projections stacked as one
+ *              [n_experts * n1, k] matrix (expert e = rows e*n1 ...), device,
+ *              16-byte aligned, tq4_fp8_cache_size(n_experts * n1, k) bytes
+ *   w2_cache : the same for the down projections, [n_experts * k, n1]
+ *   out      : [t, k] fp32, device, 16-byte aligned, overwritten
+ *   workspace: tq4_moe_grouped_fp8_workspace_size(...) bytes, device,
+ *              256-byte aligned, no initial contents required
+ * Steps: activation quantization, bucketing, grouped up projection whose
+ * epilogue squares the positive part in fp32 and quantizes it per 32-block
+ * (the quantization of tq4_act_mxfp8 on those fp32 values), grouped down
+ * projection, and the per-token weighted sum in slot order.  Deterministic.
+ * Errors: as tq4_moe_grouped, plus TQ4_E_SHAPE when t * kp, t * topk *
+ * n1p or 256 * kp reach 2^31 (kp, n1p: k, n1 padded to 128). */
+int tq4_moe_grouped_fp8(const uint16_t *x_bf16, int64_t t, int64_t k,
+                        const int32_t *topk_ids, const float *topk_w, int32_t topk,
+                        int32_t n_experts, const uint8_t *w1_cache, int64_t n1,
+                        const uint8_t *w2_cache, float *out, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* Stable bucketing of the t*topk (token, slot) pairs by expert, the routing
  * step of the sync-free MoE (model card, Running it; 128 experts, top-6 in
  * The model underneath).  Pair p = token * topk + slot.

@@ -28,6 +28,11 @@ The readings taken here:
 * y = sum_k xq[m, k] * 2^ex[m, b] * wq[n, k] * 2^ew[n, b], b = k / 32, in
   fp64.  About 63 GB for the 59 B weights of both towers matches one byte per
   weight plus one scale byte per 32 (1.03 bytes per weight).
+* the MoE layer on fp8 expert caches (the card's 128-expert top-6 MoE,
+  section The model underneath, is where most of those bytes are): both
+  projections take fp8 operands, so the hidden activations
+  h = relu(x W1^T)^2 are quantized the same way, per row and 32-block, before
+  the down projection.
 """
 
 from __future__ import annotations
@@ -47,6 +52,7 @@ __all__ = [
     "fp8_cache",
     "act_mxfp8",
     "linear_fp8",
+    "moe_fp8",
 ]
 
 E4M3_MAX = 448.0
@@ -142,3 +148,34 @@ def linear_fp8(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.
     """y = dequant(act_mxfp8(x)) . dequant(cache)^T in fp64, [M, N]."""
     xq, xs = act_mxfp8(x_bf16)
     return mx_dequant(xq, xs) @ mx_dequant(codes, scales).T
+
+
+def moe_fp8(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w1_cache, w2_cache,
+            tokens=None) -> np.ndarray:
+    """out_t = sum_j g_tj * dq(q(h_tj)) . dq(W2c_e)^T,  h_tj = relu(dq(q(x_t)) . dq(W1c_e)^T)^2,
+    e = topk_ids[t, j], q = mx_quantize, dq = mx_dequant, fp64.
+
+    ``w1_cache[e]`` is expert e's up cache (codes [n1, k], scales [n1, k/32])
+    and ``w2_cache[e]`` its down cache (codes [k, n1], scales [k, n1/32]); each
+    may be a sequence or a callable e -> (codes, scales).  Ids outside [0, E)
+    contribute nothing; ``tokens`` restricts the result to those rows.
+    """
+    xd = mx_dequant(*act_mxfp8(x_bf16))
+    ids = np.asarray(topk_ids)
+    g = np.asarray(topk_w, dtype=np.float64)
+    t_all = np.arange(xd.shape[0]) if tokens is None else np.asarray(tokens)
+    n_exp = None if callable(w1_cache) else len(w1_cache)
+    get1 = w1_cache if callable(w1_cache) else (lambda e: w1_cache[e])
+    get2 = w2_cache if callable(w2_cache) else (lambda e: w2_cache[e])
+    out = np.zeros((len(t_all), xd.shape[1]), dtype=np.float64)
+    sel = ids[t_all]
+    for e in np.unique(sel):
+        if e < 0 or (n_exp is not None and e >= n_exp):
+            continue
+        w1 = mx_dequant(*get1(int(e)))
+        w2 = mx_dequant(*get2(int(e)))
+        rows, js = np.nonzero(sel == e)
+        h = np.maximum(xd[t_all[rows]] @ w1.T, 0.0) ** 2
+        o = mx_dequant(*mx_quantize(h)) @ w2.T
+        np.add.at(out, rows, g[t_all[rows], js][:, None] * o)  # a token may list e twice
+    return out

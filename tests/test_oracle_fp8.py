@@ -128,3 +128,57 @@ def test_cache_size_matches_the_card():
     # weights of both towers: the card quotes about 63 GB
     size_gb = 59e9 * (1 + 1 / 32) / 1e9
     assert 55 < size_gb < 66
+
+
+def _exact_cache(w):
+    """Cache of an integer matrix whose 32-blocks quantize exactly."""
+    c, sc = O.mx_quantize(np.asarray(w, np.float64))
+    assert np.array_equal(O.mx_dequant(c, sc), w)
+    return c, sc
+
+
+def test_moe_fp8_exact_case_equals_integer_moe():
+    # one-hot tokens pick a column of W1, so u = W1[:, a] in {-1..3} and
+    # h = relu(u)^2 in {0, 1, 4, 9}: every quantization on the way is exact
+    # (9 * 2^5 = 288 = 1.125 * 2^8), and the layer reduces to integer
+    # arithmetic with power-of-two gates
+    rng = np.random.default_rng(5)
+    e_n, n1, k, t, topk = 5, 64, 96, 7, 2
+    w1 = rng.integers(-1, 4, size=(e_n, n1, k)).astype(np.float64)
+    w2 = rng.integers(-3, 4, size=(e_n, k, n1)).astype(np.float64)
+    cols = rng.integers(0, k, size=t)
+    x = np.zeros((t, k), np.float32)
+    x[np.arange(t), cols] = 1.0
+    ids = np.array([[0, 3], [1, 2], [4, 0], [2, 2], [3, -1], [0, 5], [1, 4]], np.int32)
+    g = np.array([[0.5, 0.25], [1, 2], [0.125, 4], [1, 1], [8, 1], [0.5, 1], [2, 0.5]])
+    want = np.zeros((t, k))
+    for ti in range(t):
+        for j in range(topk):
+            e = ids[ti, j]
+            if 0 <= e < e_n:
+                h = np.maximum(w1[e][:, cols[ti]], 0) ** 2
+                want[ti] += g[ti, j] * (w2[e] @ h)
+    got = O.moe_fp8(O.bf16_bits_from_f32(x), ids, g,
+                    [_exact_cache(w) for w in w1], [_exact_cache(w) for w in w2])
+    assert np.array_equal(got, want)
+
+
+def test_moe_fp8_rounds_the_hidden_activations():
+    # hand-derived roundings of h in one 32-block of the hidden layer:
+    #   u = 5, 1: h = 25 is the block's largest, e = -4 (25 <= 448/16 = 28 but
+    #   not <= 14); 25 * 16 = 400 lies halfway between 384 and 416 (spacing
+    #   32 in [256, 512)), the tie goes to the even code 384 -> h_q = 24.
+    #   u = 7 in another row: h = 49, e = -3, 49 * 8 = 392 -> 384 -> h_q = 48.
+    n1, k = 32, 32
+    w1 = np.zeros((n1, k))
+    w1[0, 0], w1[1, 0], w1[2, 0] = 5, 1, 3
+    w1[0, 1] = 7
+    w2 = np.eye(k, n1)                                # o = h_q itself
+    x = np.zeros((2, k), np.float32)
+    x[0, 0], x[1, 1] = 1.0, 1.0
+    ids = np.zeros((2, 1), np.int32)
+    g = np.ones((2, 1))
+    got = O.moe_fp8(O.bf16_bits_from_f32(x), ids, g, [_exact_cache(w1)], [_exact_cache(w2)])
+    assert got[0, 0] == 24.0 and got[0, 1] == 1.0 and got[0, 2] == 9.0
+    assert got[1, 0] == 48.0 and not got[1, 1:].any()
+    assert not got[0, 3:].any()
