@@ -159,7 +159,7 @@ def moe_setup(torch, np, ops, I, dev, sb, n1=1856, k=2688, n_exp=128):
     return w1, w2
 
 
-def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb):
+def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb, fp8=None):
     ids, g = I.moe_routing(wl)
     x = bf16_dev(torch, np, I.activations_bf16(wl.t, wl.k), dev)
     idt = torch.from_numpy(ids).to(dev)
@@ -186,9 +186,20 @@ def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb):
     touched = np.unique(ids).size
     per_expert = (wl.n1 * (wl.k // 32) + wl.k * (wl.n1 // 32)) * 20
     pairs = wl.t * wl.topk
-    return dict(ms_step=ms, ms_router=ms_router, ms_block=ms_block,
-                packed_bytes=touched * per_expert,
-                flops=2.0 * pairs * 2 * wl.n1 * wl.k, experts_touched=int(touched))
+    r = dict(ms_step=ms, ms_router=ms_router, ms_block=ms_block,
+             packed_bytes=touched * per_expert,
+             flops=2.0 * pairs * 2 * wl.n1 * wl.k, experts_touched=int(touched))
+    if fp8 is not None:
+        # the same layer on resident fp8 copies of the experts (tq4_moe_grouped_fp8)
+        ws8 = torch.zeros(ops.moe_grouped_fp8_workspace_size(wl.t, wl.topk, wl.n_experts, wl.n1,
+                                                             wl.k), dtype=torch.uint8, device=dev)
+        out8 = torch.empty_like(out)
+        r["ms_fp8"] = time_loop(torch, lambda i: ops.moe_grouped_fp8(
+            x, idt, gt, fp8[0], fp8[1], wl.n_experts, wl.n1, out=out8, workspace=ws8),
+            steps, warmup)
+        kp, n1p = (wl.k + 127) // 128 * 128, (wl.n1 + 127) // 128 * 128
+        r["fp8_bytes"] = touched * (wl.n1 * kp + wl.k * n1p) * 33 // 32
+    return r
 
 
 def epilogue_leg(torch, np, ops, I, wl, steps, warmup, copies, dev, sb):
@@ -368,7 +379,8 @@ def main() -> int:
             r = dense_leg(torch, np, ops, I, wl, args.steps, args.warmup, args.copies, dev, sb)
         else:
             ex = moe_setup(torch, np, ops, I, dev, sb)
-            r = moe_leg(torch, np, ops, I, wl, ex, args.steps, args.warmup, dev, sb)
+            ex8 = (ops.fp8_cache_experts(ex[0], sb), ops.fp8_cache_experts(ex[1], sb))
+            r = moe_leg(torch, np, ops, I, wl, ex, args.steps, args.warmup, dev, sb, fp8=ex8)
         log(args.only, json.dumps(r))
         if args.copy_calibration:
             src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
@@ -403,7 +415,7 @@ def main() -> int:
              ["dense_m4096_t3", "moe_t16", "moe_t1024_uniform", "moe_t1024_zipf", "pack",
               "epilogue", "fp8"]
              if args.legs == "all" else args.legs.split(","))
-    experts = None
+    experts = fp8_experts = None
     for name in names:
         if name == "pack":
             log("pack: running")
@@ -485,9 +497,12 @@ def main() -> int:
             if experts is None:
                 log("moe: generating and packing 128 experts")
                 experts = moe_setup(torch, np, ops, I, dev, sb)
+                fp8_experts = (ops.fp8_cache_experts(experts[0], sb),
+                               ops.fp8_cache_experts(experts[1], sb))
             log(f"{name}: running")
             s2 = max(5, args.steps // 10)
-            q = moe_leg(torch, np, ops, I, wl2, experts, s2, max(2, args.warmup // 5), dev, sb)
+            q = moe_leg(torch, np, ops, I, wl2, experts, s2, max(2, args.warmup // 5), dev, sb,
+                        fp8=fp8_experts)
             g2 = q["packed_bytes"] / (q["ms_step"] * 1e-3) / 1e9
             tf = q["flops"] / (q["ms_step"] * 1e-3) / 1e12
             legs[name] = {"ms_per_step": round(q["ms_step"], 4), "GB/s": round(g2, 1),
@@ -496,7 +511,13 @@ def main() -> int:
                           "block_from_logits_us": round(q["ms_block"] * 1e3, 2),
                           "roofline": {"bound": "hbm", "achieved": round(g2, 1),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": round(g2 / HBM_PEAK_GBS, 4)}}
+                                       "frac": round(g2 / HBM_PEAK_GBS, 4)},
+                          "fp8_cache": {
+                              "what": "the same layer on resident MXFP8 expert copies "
+                                      "(tq4_moe_grouped_fp8), GB/s on their touched bytes",
+                              "ms_per_step": round(q["ms_fp8"], 4),
+                              "GB/s": round(q["fp8_bytes"] / (q["ms_fp8"] * 1e-3) / 1e9, 1),
+                              "time_over_tq4": round(q["ms_fp8"] / q["ms_step"], 3)}}
         log(name, json.dumps(legs[name]))
 
     cpu = None

@@ -233,6 +233,36 @@ def test_moe_block_argument_errors(L):
     assert call(t=0) == OK
 
 
+def test_moe_grouped_fp8_argument_errors(L):
+    ws = L.tq4_moe_grouped_fp8_workspace_size(16, 6, 128, 1856, 2688)
+    # route lists, 16-row tiles, xq/xs (kp 2688), hq/hs (n1p 1920), fp32 o
+    assert ws >= 16 * 2688 * 33 // 32 + 96 * 1920 * 33 // 32 + 96 * 2688 * 4
+    assert L.tq4_moe_grouped_fp8_workspace_size(16, 6, 128, 1850, 2688) == 0   # n1 % 32
+    assert L.tq4_moe_grouped_fp8_workspace_size(16, 7, 4, 64, 64) == 0         # topk > E
+    assert L.tq4_moe_grouped_fp8_workspace_size(1 << 20, 6, 128, 1856, 2688) == 0  # t * kp
+
+    def call(**kw):
+        a = dict(dict(x=FAKE, t=16, k=2688, ids=FAKE, g=FAKE, topk=6, e=128, w1=FAKE, n1=1856,
+                      w2=FAKE, out=FAKE, ws=FAKE, wsb=ws), **kw)
+        return L.tq4_moe_grouped_fp8(a["x"], a["t"], a["k"], a["ids"], a["g"], a["topk"], a["e"],
+                                     a["w1"], a["n1"], a["w2"], a["out"], a["ws"], a["wsb"], None)
+
+    assert call(topk=129) == E_SHAPE
+    assert call(e=513) == E_SHAPE
+    assert call(n1=1850) == E_SHAPE
+    assert call(k=2690) == E_SHAPE
+    assert call(ids=None) == E_NULL
+    assert call(w2=None) == E_NULL
+    assert call(out=None) == E_NULL
+    assert call(g=FAKE + 2) == E_ALIGN
+    assert call(w1=FAKE + 4) == E_ALIGN
+    assert call(x=MIS) == E_ALIGN
+    assert call(ws=None) == E_WS
+    assert call(wsb=ws - 1) == E_WS
+    assert call(ws=FAKE + 16) == E_ALIGN
+    assert call(t=0) == OK
+
+
 def test_moe_argument_errors(L):
     ws = L.tq4_moe_workspace_size(16, 6, 128, 1856, 2688)
     assert ws > 0
