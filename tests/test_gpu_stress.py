@@ -86,10 +86,15 @@ def test_moe_repeated(dev):
         return torch.from_numpy(raw).to(dev)
     w1 = experts(n1, k)
     w2 = experts(k, n1)
+    c1 = _ops().fp8_cache_experts(w1, SB)
+    c2 = _ops().fp8_cache_experts(w2, SB)
     calls = []
     for name in ("moe_t16", "moe_t1024_zipf"):
         wl = I.WORKLOADS[name]
         lg = torch.from_numpy(I.router_logits(wl.t, wl.n_experts, wl.routing).astype(np.float32)).to(dev)
         x = _bf16(I.activations_bf16(wl.t, wl.k), dev)
+        ids, g = (torch.from_numpy(a).to(dev) for a in I.moe_routing(wl))
         calls.append(lambda x=x, lg=lg, wl=wl: _ops().moe_block(x, lg, wl.topk, w1, w2, SB))
+        # the fp8 layer's stage waits and fused hidden quantization
+        calls.append(lambda x=x, ids=ids, g=g: _ops().moe_grouped_fp8(x, ids, g, c1, c2, e, n1))
     _repeat(calls, 10)
