@@ -198,6 +198,24 @@ def test_moe_fp8_small_matches_oracle(dev, t, n_exp, topk, n1, k):
     _check_bracket(out, x, ids, g, c1, c2, np.arange(t), f"fp8 moe t{t} E{n_exp} {n1}x{k}")
 
 
+@pytest.mark.parametrize("t,n_exp,topk,n1,k,hot", [
+    (300, 2, 1, 96, 160, 0),     # every token on expert 0: three 128-row tiles, the last partial
+    (50, 64, 2, 64, 96, 5),      # slot 0 always expert 5: four 16-row tiles of one expert
+])
+def test_moe_fp8_one_popular_expert(dev, t, n_exp, topk, n1, k, hot):
+    ex = _small_experts(dev, n_exp, n1, k, seed=hot + 11)
+    rng = np.random.default_rng(hot)
+    ids = np.full((t, topk), hot, np.int32)
+    if topk > 1:
+        others = np.array([e for e in range(n_exp) if e != hot])
+        ids[:, 1:] = rng.choice(others, size=(t, topk - 1))
+    g = rng.random((t, topk)).astype(np.float32)
+    x = I.activations_bf16(t, k, seed=hot + 1)
+    out = _run(dev, ex, x, ids, g)
+    c1, c2 = ex.oracle(np.unique(ids))
+    _check_bracket(out, x, ids, g, c1, c2, np.arange(t), f"fp8 moe hot expert {hot}, t{t}")
+
+
 def test_moe_fp8_invalid_and_repeated_ids(dev):
     t, n_exp, topk, n1, k = 33, 6, 3, 128, 128
     ex = _small_experts(dev, n_exp, n1, k, seed=9)
