@@ -587,25 +587,41 @@ def test_graph_replays_match_eager(dev, experts):
     ws_lin = torch.zeros(ops.linear_workspace_size(100, 2688, 8192), dtype=torch.uint8, device=dev)
     ws_moe = torch.zeros(ops.moe_workspace_size(wl.t, 6, 128, 1856, 2688), dtype=torch.uint8,
                          device=dev)
+    # the fp8 variants: dense at M=16 and M=100, and the MoE layer
+    c = ops.fp8_cache(p, SB)
+    c1, c2 = ops.fp8_cache_experts(experts[0], SB), ops.fp8_cache_experts(experts[1], SB)
+    f16 = torch.empty((16, 8192), device=dev)
+    f100 = torch.empty((100, 8192), device=dev)
+    fm = torch.empty((wl.t, wl.k), device=dev)
+    ws_f16 = torch.zeros(ops.linear_fp8_workspace_size(16, 2688, 8192), dtype=torch.uint8,
+                         device=dev)
+    ws_f100 = torch.zeros(ops.linear_fp8_workspace_size(100, 2688, 8192), dtype=torch.uint8,
+                          device=dev)
+    ws_fm = torch.zeros(ops.moe_grouped_fp8_workspace_size(wl.t, 6, 128, 1856, 2688),
+                        dtype=torch.uint8, device=dev)
+    outs = (y16, y100, om, f16, f100, fm)
 
     def run():
         ops.linear(x16, p, SB, out=y16)
         ops.linear(x100, p, SB, out=y100, workspace=ws_lin)
         ops.moe_grouped(xm, idt, gt, experts[0], experts[1], SB, out=om, workspace=ws_moe)
+        ops.linear_fp8(x16, c, 8192, out=f16, workspace=ws_f16)
+        ops.linear_fp8(x100, c, 8192, out=f100, workspace=ws_f100)
+        ops.moe_grouped_fp8(xm, idt, gt, c1, c2, 128, 1856, out=fm, workspace=ws_fm)
 
     run()
     torch.cuda.synchronize()
-    ref = [y16.clone(), y100.clone(), om.clone()]
+    ref = [t.clone() for t in outs]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         run()
     for rep in range(3):
-        for t in (y16, y100, om):
+        for t in outs:
             t.fill_(float("nan"))
         junk = ops.linear(x100, p, SB)          # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.isfinite(junk).all()
-        for a, b in zip((y16, y100, om), ref):
-            assert torch.equal(a, b), rep
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), (rep, i)
