@@ -208,8 +208,8 @@ hipError_t launch_act_mxfp8_f32(const float *x, int64_t m, int64_t k, uint8_t *c
 // perm[row] / topk from aq [a_rows][kp]; writes MXFP8 codes and scale bytes of
 // relu(acc)^2 into hq [pairs][n_store], hs [pairs][n_store / 32] (n_store =
 // hidden width padded to 128).  mode 1 (down): activation rows are the bucket
-// rows of aq; out[row][n] = acc (fp32).  tile_rows: 16, 64 or 128 (as given
-// to launch_route).
+// rows of aq; out[row][n] = acc (fp32).  tile_rows: 16 or 64 (as given to
+// launch_route).
 int fp8_moe_tile_rows(int64_t pairs, int32_t n_experts);
 bool fp8_moe_shape_fits(int64_t a_rows, int64_t k, int64_t n);
 hipError_t launch_moe_fp8(int mode, int tile_rows, const uint8_t *aq, const uint8_t *as,

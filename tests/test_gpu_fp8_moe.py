@@ -183,9 +183,9 @@ def _run(dev, ex, x, ids, g):
 
 @pytest.mark.parametrize("t,n_exp,topk,n1,k", [
     (40, 16, 2, 224, 352),    # 16-row tiles; ragged hidden and model widths
-    (300, 4, 2, 160, 288),    # 128-row tiles, two per expert
+    (300, 4, 2, 160, 288),    # 64-row tiles, three per expert
     (1, 3, 1, 32, 32),        # one pair, one 32-block each way
-    (70, 5, 3, 128, 640),     # 128-row tiles, one partial per expert
+    (70, 5, 3, 128, 640),     # 64-row tiles, a full and a partial one per expert
 ])
 def test_moe_fp8_small_matches_oracle(dev, t, n_exp, topk, n1, k):
     ex = _small_experts(dev, n_exp, n1, k, seed=t + n_exp)
@@ -199,7 +199,7 @@ def test_moe_fp8_small_matches_oracle(dev, t, n_exp, topk, n1, k):
 
 
 @pytest.mark.parametrize("t,n_exp,topk,n1,k,hot", [
-    (300, 2, 1, 96, 160, 0),     # every token on expert 0: three 128-row tiles, the last partial
+    (300, 2, 1, 96, 160, 0),     # every token on expert 0: five 64-row tiles, the last partial
     (50, 64, 2, 64, 96, 5),      # slot 0 always expert 5: four 16-row tiles of one expert
 ])
 def test_moe_fp8_one_popular_expert(dev, t, n_exp, topk, n1, k, hot):
@@ -244,7 +244,7 @@ def test_moe_fp8_full_size_sampled_tokens(dev, full_experts, name):
     x = I.activations_bf16(wl.t, wl.k)
     out = _run(dev, full_experts, x, ids, g)
     assert np.isfinite(out).all()
-    # tokens of the hottest expert (several 128-row tiles under Zipf routing)
+    # tokens of the hottest expert (13 64-row tiles under Zipf routing)
     # plus a spread sample
     hot = np.bincount(ids.reshape(-1), minlength=wl.n_experts).argmax()
     tok = np.unique(np.concatenate([np.nonzero((ids == hot).any(1))[0][:3],
