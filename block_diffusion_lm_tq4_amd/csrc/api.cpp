@@ -47,6 +47,8 @@ int check_workspace(const void *ws, size_t bytes, size_t need) {
   return TQ4_OK;
 }
 
+constexpr int64_t kFusedRouterTokens = 64;
+
 // ---- tq4_moe_grouped workspace ------------------------------------------
 struct MoELayout {
   size_t counts, offsets, perm, inv, tiles, meta, xt, ht, o, total;
@@ -258,11 +260,13 @@ size_t tq4_moe_workspace_size(int64_t t, int32_t topk, int32_t n_experts, int64_
 namespace {
 
 // The layer after validation: workspace of at least moe_layout(...).total
-// bytes, 256-byte aligned.
+// bytes, 256-byte aligned.  With logits != nullptr the bucketing launch also
+// routes the tokens, writing topk_ids and topk_w (then writable).
 hipError_t moe_layer(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t *topk_ids,
                      const float *topk_w, int32_t topk, int32_t n_experts,
                      const uint8_t *w1_packed, int64_t n1, const uint8_t *w2_packed,
-                     uint32_t sign_bits, float *out, char *ws, hipStream_t s) {
+                     uint32_t sign_bits, float *out, char *ws, hipStream_t s,
+                     const float *logits = nullptr) {
   const MoEPlan p = tq4::plan_moe(t * topk, n_experts);
   const MoELayout l = moe_layout(t, topk, n_experts, n1, k, p);
   int32_t *counts = reinterpret_cast<int32_t *>(ws + l.counts);
@@ -277,7 +281,7 @@ hipError_t moe_layer(const uint16_t *x_bf16, int64_t t, int64_t k, const int32_t
   const int64_t pairs = t * topk;
   hipError_t e = tq4::launch_route(topk_ids, pairs, topk, n_experts, counts, offsets, perm, inv,
                                    tiles, meta, p.tile_rows, nullptr, s, x_bf16, t * (k / 32),
-                                   sign_bits, xt);
+                                   sign_bits, xt, logits, const_cast<float *>(topk_w));
   if (e == hipSuccess)
     e = tq4::launch_moe_gemm(p, 0, xt, k, perm, topk, w1_packed, n1, tiles, meta, nullptr, ht,
                              sign_bits, s);
@@ -348,6 +352,12 @@ int tq4_moe_block(const uint16_t *x_bf16, int64_t t, int64_t k, const float *log
   int32_t *ids = reinterpret_cast<int32_t *>(ws + layer);
   float *gates = reinterpret_cast<float *>(ws + layer + align_up(slots * sizeof(int32_t)));
   hipStream_t s = as_stream(stream);
+  // up to 64 tokens (4 per wave of the bucketing workgroup) the router runs
+  // inside the bucketing launch; above that as its own launch of t / 4
+  // workgroups.  Both use the same per-token routine: the same ids and gates.
+  if (t <= kFusedRouterTokens)
+    return device_status(moe_layer(x_bf16, t, k, ids, gates, topk, n_experts, w1_packed, n1,
+                                   w2_packed, sign_bits, out, ws, s, logits));
   hipError_t e = tq4::launch_router(logits, t, n_experts, topk, ids, gates, s);
   if (e == hipSuccess)
     e = moe_layer(x_bf16, t, k, ids, gates, topk, n_experts, w1_packed, n1, w2_packed, sign_bits,

@@ -25,6 +25,61 @@ __device__ inline uint64_t same_key_lanes(int key, uint64_t active, int key_bits
   return m;
 }
 
+// The router in front of the layer (model card, The model underneath: 128
+// experts, top-6) for one token, by one wave: softmax over all expert logits,
+// then the topk largest logits with ties to the lower expert id, each gate the
+// expert's softmax probability (not renormalized).  Lane l holds experts
+// l, l + 64, ...; the max, the sum and every arg-max are xor-butterfly
+// reductions, which leave bit-identical results in all lanes.
+constexpr int kRouterPer = kMaxExperts / 64;
+
+__device__ inline void route_one_token(const float *row, int32_t n_experts, int32_t topk,
+                                       int lane, int32_t *ids, float *gates) {
+  float v[kRouterPer];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < kRouterPer; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < n_experts ? row[e] : -__builtin_inff();
+    mx = fmaxf(mx, v[i]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRouterPer; ++i)
+    if (lane + 64 * i < n_experts) sum += expf(v[i] - mx);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+  uint32_t taken = 0;
+  for (int j = 0; j < topk; ++j) {
+    float bv = -__builtin_inff();
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kRouterPer; ++i) {
+      const int e = lane + 64 * i;
+      if (e < n_experts && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const float ov = __shfl_xor(bv, d);
+      const int oi = __shfl_xor(bi, d);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == bi % 64) taken |= 1u << (bi / 64);
+    if (lane == 0) {
+      ids[j] = bi;
+      gates[j] = expf(bv - mx) / sum;
+    }
+  }
+}
+
 // One workgroup.  Pairs are split into kRouteWaves contiguous ranges, one per
 // wave, walked in batches of 64 in pair order:
 //   pass 1  per-wave expert histograms (LDS);
@@ -32,11 +87,15 @@ __device__ inline uint64_t same_key_lanes(int key, uint64_t active, int key_bits
 //   pass 2  each pair's slot = offsets[e] + (pairs of e in earlier waves)
 //           + (pairs of e earlier in this wave), the last term from ballots.
 // This is a stable counting sort: inside an expert, pairs keep their order.
+// With logits != nullptr the workgroup first routes the pairs / topk tokens
+// itself (one wave per token, route_one_token) into ids and gates, which the
+// bucketing then reads back.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const int32_t *__restrict__ ids, int64_t pairs, int32_t n_experts, int32_t *counts,
+    int32_t *ids, int64_t pairs, int32_t n_experts, int32_t *counts,
     int32_t *offsets, int32_t *perm, int32_t *inv, MoETile *tiles, int32_t *n_tiles,
     int32_t tile_rows, int32_t *status, const uint16_t *__restrict__ x, int64_t x_blocks,
-    uint32_t sign_bits, uint16_t *__restrict__ xt) {
+    uint32_t sign_bits, uint16_t *__restrict__ xt, const float *__restrict__ logits,
+    int32_t topk, float *gates) {
   __shared__ int32_t hist[kRouteWaves][kMaxExperts];
   __shared__ int32_t base[kMaxExperts + 1];
   __shared__ int32_t tile_base[kMaxExperts + 1];
@@ -50,6 +109,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   }
   const int wave = tid / 64;
   const int lane = tid % 64;
+  if (logits != nullptr) {
+    for (int64_t tok = wave; tok < pairs / topk; tok += kRouteWaves)
+      route_one_token(logits + tok * n_experts, n_experts, topk, lane, ids + tok * topk,
+                      gates + tok * topk);
+    __threadfence();
+    __syncthreads();  // the ids are in memory for every wave
+  }
   int key_bits = 0;
   while ((1 << key_bits) < n_experts) ++key_bits;
 
@@ -192,65 +258,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   }
 }
 
-// The router in front of the layer (model card, The model underneath: 128
-// experts, top-6), one wave per token: softmax over all expert logits, then
-// the topk largest logits with ties to the lower expert id, each gate the
-// expert's softmax probability (not renormalized).  Lane l holds experts
-// l, l + 64, ...; the max, the sum and every arg-max are xor-butterfly
-// reductions, which leave bit-identical results in all lanes.
-constexpr int kRouterPer = kMaxExperts / 64;
-
+// The router in front of the layer, one wave per token (route_one_token).
 __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ logits, int64_t t,
                                                      int32_t n_experts, int32_t topk,
                                                      int32_t *__restrict__ ids,
                                                      float *__restrict__ gates) {
   const int64_t tok = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
   if (tok >= t) return;
-  const int lane = threadIdx.x % 64;
-  const float *row = logits + tok * n_experts;
-  float v[kRouterPer];
-  float mx = -__builtin_inff();
-#pragma unroll
-  for (int i = 0; i < kRouterPer; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < n_experts ? row[e] : -__builtin_inff();
-    mx = fmaxf(mx, v[i]);
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < kRouterPer; ++i)
-    if (lane + 64 * i < n_experts) sum += expf(v[i] - mx);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
-  uint32_t taken = 0;
-  for (int j = 0; j < topk; ++j) {
-    float bv = -__builtin_inff();
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kRouterPer; ++i) {
-      const int e = lane + 64 * i;
-      if (e < n_experts && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d);
-      const int oi = __shfl_xor(bi, d);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (lane == bi % 64) taken |= 1u << (bi / 64);
-    if (lane == 0) {
-      ids[tok * topk + j] = bi;
-      gates[tok * topk + j] = expf(bv - mx) / sum;
-    }
-  }
+  route_one_token(logits + tok * n_experts, n_experts, topk, threadIdx.x % 64, ids + tok * topk,
+                  gates + tok * topk);
 }
 
 }  // namespace
@@ -259,13 +275,16 @@ hipError_t launch_route(const int32_t *ids, int64_t pairs, int32_t topk, int32_t
                         int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                         MoETile *tiles, int32_t *n_tiles, int32_t tile_rows, int32_t *status,
                         hipStream_t s, const uint16_t *x, int64_t x_blocks, uint32_t sign_bits,
-                        uint16_t *xt) {
-  (void)topk;
+                        uint16_t *xt, const float *logits, float *gates) {
   if (n_experts > kMaxExperts) return hipErrorInvalidValue;
+  if (logits != nullptr && (gates == nullptr || topk < 1 || pairs % topk != 0))
+    return hipErrorInvalidValue;
   const int64_t rot_wgs = x != nullptr ? (x_blocks + kRouteThreads - 1) / kRouteThreads : 0;
+  // the ids are written by the kernel itself when it also routes
   hipLaunchKernelGGL(route_kernel, dim3(static_cast<unsigned>(1 + rot_wgs)), dim3(kRouteThreads),
-                     0, s, ids, pairs, n_experts, counts, offsets, perm, inv, tiles, n_tiles,
-                     tile_rows, status, x, x_blocks, sign_bits, xt);
+                     0, s, const_cast<int32_t *>(ids), pairs, n_experts, counts, offsets, perm,
+                     inv, tiles, n_tiles, tile_rows, status, x, x_blocks, sign_bits, xt, logits,
+                     topk, gates);
   return hipGetLastError();
 }
 

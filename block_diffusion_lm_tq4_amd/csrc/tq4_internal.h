@@ -165,12 +165,15 @@ struct MoETile {  // one m-tile of one expert's segment in bucket order
 };
 // Bucketing (one workgroup).  With x != nullptr the same launch also rotates
 // the [t, k] bf16 activation rows into xt (extra workgroups, one thread per
-// 32-block).
+// 32-block).  With logits != nullptr the bucketing workgroup first routes the
+// pairs / topk tokens itself (the router's arithmetic, bit for bit), writing
+// ids (then writable device memory) and gates.
 hipError_t launch_route(const int32_t *ids, int64_t pairs, int32_t topk, int32_t n_experts,
                         int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                         MoETile *tiles, int32_t *n_tiles, int32_t tile_rows,
                         int32_t *status, hipStream_t s, const uint16_t *x = nullptr,
-                        int64_t x_blocks = 0, uint32_t sign_bits = 0, uint16_t *xt = nullptr);
+                        int64_t x_blocks = 0, uint32_t sign_bits = 0, uint16_t *xt = nullptr,
+                        const float *logits = nullptr, float *gates = nullptr);
 
 struct MoEPlan {
   int msub, nsub, waves_m, waves_n;
