@@ -113,8 +113,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     for (int64_t tok = wave; tok < pairs / topk; tok += kRouteWaves)
       route_one_token(logits + tok * n_experts, n_experts, topk, lane, ids + tok * topk,
                       gates + tok * topk);
-    __threadfence();
-    __syncthreads();  // the ids are in memory for every wave
+    // the ids are read back only by this workgroup's waves (one compute
+    // unit): a workgroup-scope fence and the barrier make them visible
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __syncthreads();
   }
   int key_bits = 0;
   while ((1 << key_bits) < n_experts) ++key_bits;
