@@ -31,8 +31,9 @@
 // MoE.  The same core runs over a device-built list of (expert, first row,
 // rows) tiles.  Mode up gathers activation rows through the bucket
 // permutation and stores relu(acc)^2 already rotated for the down
-// projection (fp16, one 32-block per wave); mode down reads the bucketed hidden
-// rows and stores acc.  Tiles past the device-side count exit at once, so the
+// projection (fp16, one 32-block per wave, scaled by 2^-kHiddenShift to keep
+// large hidden values in fp16's range); mode down reads the bucketed hidden
+// rows and stores acc with both shifts undone.  Tiles past the device-side count exit at once, so the
 // grid is sized on the host from t*topk without a sync.
 #include "tq4_internal.h"
 
@@ -134,7 +135,9 @@ __device__ inline void store_tiles_impl(const floatx4 (&acc)[MS][NS], float *out
       for (int j = 0; j < NS; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float a = acc[i0 + ii][j][v];  // the same two adds, in order, as tail_sum
+          // the weight shift undone (exact), then the same two adds, in
+          // order, as tail_sum
+          float a = acc[i0 + ii][j][v] * kWeightUnscale;
           if (t.bias != nullptr) a += bv[j];
           if (t.residual != nullptr) a += y[ii][j][v];
           y[ii][j][v] = a;
@@ -174,8 +177,10 @@ __device__ inline void store_tiles(const floatx4 (&acc)[MS][NS], float *out, con
   }
 }
 
+// The half-block scale as an fp16 pair, shifted by 2^kWeightShift (exact;
+// the shift is undone on the fp32 results, see tq4_internal.h).
 __device__ inline half2v scale_pair(uint32_t bf16_bits) {
-  const _Float16 h = static_cast<_Float16>(__uint_as_float(bf16_bits << 16));
+  const _Float16 h = static_cast<_Float16>(__uint_as_float(bf16_bits << 16) * kWeightScale);
   half2v r;
   r[0] = h;
   r[1] = h;
@@ -388,7 +393,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
     // lanes per staged row rotate it in registers: lane parity p holds
     // elements 16p .. 16p + 15, rotated in-lane over bits 0-3 of the element
     // index, and bit 4 pairs the two lanes (a quad-permute exchange).  Each
-    // lane writes 32 contiguous bytes.
+    // lane writes 32 contiguous bytes.  The stored values carry the factor
+    // 2^-kHiddenShift, which the down product's result undoes.
     static_assert(NSUB == 2, "one 32-block of hidden units per wave");
     static_assert(kWaves * 8 * MSUB * 32 * 4 <= TM * kChunkBytes, "staging fits");
     __syncthreads();  // every wave is done with the activation stages
@@ -402,14 +408,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float u = acc[i][j][v];
+            const float u = acc[i][j][v] * kWeightUnscale;
             const int srow = 8 * i + 4 * (grp & 1) + v;
             hw[srow * 32 + ((16 * j + r) ^ (4 * ((srow >> 1) & 7)))] = u > 0.f ? u * u : 0.f;
           }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own writes are visible
     const int64_t col0 = n_base + wave * 32;
-    const float rs32 = 0x1.6a09e6p-3f;
+    const float rs32 = kHiddenRotScale;  // 1/sqrt(32) and the hidden shift
     const int p = lane & 1;
     const int srow = (lane >> 1) < 8 * MSUB ? (lane >> 1) : 0;
     const int key = 4 * ((srow >> 1) & 7);
@@ -471,7 +477,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int64_t local = 16 * i + 4 * grp + v;
-          if (local < rows_valid && n < g.n) g.out[(m_base + local) * g.n + n] = acc[i][j][v];
+          if (local < rows_valid && n < g.n)
+            g.out[(m_base + local) * g.n + n] = acc[i][j][v] * kHiddenUnscale;
         }
       }
   }

@@ -24,10 +24,11 @@
 //  1. rotates the chunk's 4 activation blocks from LDS:
 //     xt_b = H32 diag(s) x_b / sqrt(32) is a product with a +-1 matrix, so two
 //     v_mfma_f32_16x16x32_bf16 per block compute it from the bf16 input
-//     (products by +-1 are exact, sums are fp32).  The MFMA rows are permuted
-//     so that lane group g receives xt elements 8g..8g+7 of the block: that is
-//     directly the activation operand of the block's product MFMA.  The
-//     1/sqrt(32) is applied once to y;
+//     against entries +-2^-3 (exact in bf16; products exact, sums fp32).  The
+//     MFMA rows are permuted so that lane group g receives xt elements
+//     8g..8g+7 of the block: that is directly the activation operand of the
+//     block's product MFMA.  The remaining 8/sqrt(32) is applied once to y
+//     (with the weight operand's 2^-8, see tq4_internal.h);
 //  2. transposes its weight words across the 4 lane groups (lane group g
 //     loaded block 4c+g; after two v_permlane32_swap and two
 //     v_permlane16_swap per 4 words it holds word g of every block), so that
@@ -90,8 +91,9 @@ __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *l
   return r;
 }
 
+// The half-block scale as an fp16 pair, shifted by 2^kWeightShift (exact).
 __device__ inline half2v scale_pair(uint32_t bf16_bits) {
-  const float f = __uint_as_float(bf16_bits << 16);
+  const float f = __uint_as_float(bf16_bits << 16) * kWeightScale;
   return __builtin_convertvector((float2v){f, f}, half2v);
 }
 
@@ -192,8 +194,8 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
       const uint32_t sk = (g.sign_bits >> kk) & 1u;
       const uint32_t n_lo = (__builtin_popcount(j_lo & kk) & 1) ^ sk;
       const uint32_t n_hi = (__builtin_popcount((j_lo + 4) & kk) & 1) ^ sk;
-      h_lo[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x3F80u | (n_lo << 15)));
-      h_hi[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x3F80u | (n_hi << 15)));
+      h_lo[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(kRotEntryBF16 | (n_lo << 15)));
+      h_hi[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(kRotEntryBF16 | (n_hi << 15)));
     }
   }
   __builtin_amdgcn_s_barrier();  // 0
@@ -269,11 +271,10 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
     for (int w = 1; w < kConsumers; ++w) s += red[w][wave][lane];
     const int n = n_base + 16 * wave;
     if (n < g.n) {
-      const float rs32 = 0x1.6a09e6p-3f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * grp + v;
-        if (m < g.m) tail_apply(g.tail, g.y, m, n, g.n, s[v] * rs32);
+        if (m < g.m) tail_apply(g.tail, g.y, m, n, g.n, s[v] * kSkinnyUnscale);
       }
     }
   }
@@ -313,7 +314,6 @@ constexpr int kDmaMaxChunks = kDmaMaxK / 128;               // 23
 // interleaved ones (7.4 against 7.6 us per call).
 constexpr int kDmaLutCopies = 1;
 
-typedef __attribute__((address_space(3))) volatile uint32_t lds_flag;
 
 __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t slots[kDmaMaxChunks * kSlotBytes];
@@ -413,8 +413,8 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
       const uint32_t sk = (g.sign_bits >> kk) & 1u;
       const uint32_t n_lo = (__builtin_popcount(j_lo & kk) & 1) ^ sk;
       const uint32_t n_hi = (__builtin_popcount((j_lo + 4) & kk) & 1) ^ sk;
-      h_lo[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x3F80u | (n_lo << 15)));
-      h_hi[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x3F80u | (n_hi << 15)));
+      h_lo[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(kRotEntryBF16 | (n_lo << 15)));
+      h_hi[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(kRotEntryBF16 | (n_hi << 15)));
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): flags and pair table written
@@ -431,7 +431,10 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
   // of one round trip per block: what bounds a consumer is LDS latency, and
   // the last chunk's latency is the kernel's tail.
   for (int c = wave; c < chunks; c += kDmaConsumers) {
-    while (*(lds_flag *)(&ready[c]) == 0u) __builtin_amdgcn_s_sleep(1);
+    // acquire at workgroup scope: the slot reads below cannot move above the
+    // load that saw the flag set
+    while (__hip_atomic_load(&ready[c], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
+      __builtin_amdgcn_s_sleep(1);
     const uint8_t *sl = slots + c * kSlotBytes;
     // 1. this lane's x parts, code words and half-block scales
     bf16x8 xb[4];
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
     for (int w = 1; w < kDmaConsumers; ++w) sum += red[((w * kRowTiles + j) * 4 + v) * 64 + lane];
     const int n = n0 + r + 16 * j;
     const int m = 4 * grp + v;
-    if (n < g.n && m < g.m) tail_apply(g.tail, g.y, m, n, g.n, sum * 0x1.6a09e6p-3f);
+    if (n < g.n && m < g.m) tail_apply(g.tail, g.y, m, n, g.n, sum * kSkinnyUnscale);
   }
 }
 

@@ -14,6 +14,33 @@ struct Codebook {
 // Lloyd-Max levels of N(0,1) rounded to fp32, computed once on the host.
 const Codebook &codebook();
 
+// fp16 operand range.  The products take 16-bit operands (fp16 keeps 11
+// significant bits, which the error bar needs; its exponent spans only
+// 2^-14 .. 65504), so the values entering them are shifted by exact powers
+// of two and the shifts are undone on the fp32 results:
+//  * weight operand: S * c * 2^kWeightShift.  Half-block scales S from about
+//    2e-6 to 93.6 then give normal fp16 values (a bf16 scale is exact in fp16
+//    there), instead of 5e-4 to 2.4e4 unshifted: weights down to an rms of
+//    about 1e-6 keep full precision, and blocks whose rotated values stay
+//    below 255 cannot overflow;
+//  * MoE hidden rows: R relu(u)^2 * 2^-kHiddenShift, so that |u| up to about
+//    430 fits (the square doubles the exponent range of u);
+//  * the M <= 16 kernels rotate with +-2^-3 entries (exact in bf16) and fold
+//    the 8 into the final 1/sqrt(32): a 32-block sum reaches fp16's limit
+//    only at |sum of +-x| = 8 * 65504.
+constexpr int kWeightShift = 8;
+constexpr float kWeightScale = 256.0f;         // 2^kWeightShift
+constexpr float kWeightUnscale = 0x1p-8f;      // 2^-kWeightShift
+constexpr int kHiddenShift = 4;
+// 1/sqrt(32) * 2^-kHiddenShift (fp32; the power of two is exact)
+constexpr float kHiddenRotScale = 0x1.6a09e6p-7f;
+// the down product's result: 2^(kHiddenShift - kWeightShift)
+constexpr float kHiddenUnscale = 0x1p-4f;
+// M <= 16 kernels: sum * 8 / sqrt(32) * 2^-kWeightShift = sum * fp32(sqrt 2) * 2^-8
+constexpr float kSkinnyUnscale = 0x1.6a09e6p-8f;
+// bf16 bits of +-2^-3, the entries of the M <= 16 kernels' rotation operand
+constexpr uint16_t kRotEntryBF16 = 0x3E00u;
+
 // xt = H32 diag(s) x / sqrt(32) of one 32-element block: bf16 in (16-byte
 // aligned), fp32 butterfly in natural (Sylvester) order, fp16 out.  The format
 // rotates every weight block by this orthogonal matrix (Nemotron-TheHobbit-

@@ -31,6 +31,27 @@
  *     any GPU work is enqueued.  A failed launch returns TQ4_E_DEVICE.
  *   - Outputs are overwritten, never accumulated into.
  *   - Two calls that share a workspace must not run concurrently.
+ *
+ * Numeric range of the TQ4_1S products (tq4_linear*, tq4_moe_*).  They
+ * multiply 16-bit fp16 operands with fp32 accumulation; fp16 has 11
+ * significant bits (the error bar below needs them) but an exponent range of
+ * 2^-14 .. 65504 only, so every operand is shifted by an exact power of two
+ * that the fp32 result undoes.  Inside this domain each output meets
+ * relative Frobenius error <= 2e-3 and max |error| <= 1e-2 * rms(y) against
+ * the exact product of the decoded weights:
+ *   - weights: every half-block scale S <= 93.6, i.e. every rotated block
+ *     value |z| <= 255 (guaranteed when every |w| <= 45).  Scales below about
+ *     2e-6 (weights of rms below about 3e-6) lose precision gradually to
+ *     fp16 subnormals rather than failing;
+ *   - activations: for every 32-block of a row, |sum_i +-x_i| < 370000 over
+ *     every sign pattern (guaranteed when every |x| <= 11579).  Rows whose
+ *     rotated values are all below about 6e-5 lose precision gradually;
+ *   - MoE hidden rows: the up products u satisfy, per 32-block,
+ *     |sum_i +-relu(u_i)^2| < 5.9e6 (guaranteed when every |u| <= 430);
+ *     rows whose squares are all below about 1e-3 lose precision gradually.
+ * Outside it an output may be less accurate or infinite; nothing is checked
+ * on the device (no host synchronization).  The fp8 entry points use MXFP8
+ * operands with their own per-block exponents and have no such limit.
  */
 #ifndef TQ4_H
 #define TQ4_H

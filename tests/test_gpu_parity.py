@@ -539,6 +539,39 @@ def test_moe_block_matches_oracle_and_the_two_calls(dev, experts, name):
     _check_close(out.cpu().numpy()[tokens], ref, f"moe block {name}")
 
 
+@pytest.mark.parametrize("t,e,topk", [
+    (17, 128, 6),    # the router inside the bucketing launch: 2 tokens per wave
+    (64, 128, 6),    # its limit: 4 tokens per wave
+    (65, 128, 6),    # past it: the separate router launch
+    (40, 100, 4),    # experts not a multiple of 64
+    (64, 100, 8),
+])
+def test_moe_block_router_placements(dev, t, e, topk):
+    """tq4_moe_block equals tq4_moe_router + tq4_moe_grouped bit for bit on
+    both sides of the fused-router limit and for expert counts that do not
+    fill a wave, and matches the oracle's router + layer."""
+    rng = np.random.default_rng(t * 131 + e)
+    k, n1 = 96, 64
+    w1 = (0.05 * rng.standard_normal((e, n1, k))).astype(np.float32)
+    w2 = (0.05 * rng.standard_normal((e, k, n1))).astype(np.float32)
+    p1 = np.stack([O.pack(w1[i], SB) for i in range(e)])
+    p2 = np.stack([O.pack(w2[i], SB) for i in range(e)])
+    lg = I.router_logits(t, e, "zipf", seed=t).astype(np.float32)
+    x_bits = I.activations_bf16(t, k, seed=t + 1)
+    xb = _bf16(x_bits, dev)
+    lg_d = torch.from_numpy(lg).to(dev)
+    p1d, p2d = torch.from_numpy(p1).to(dev), torch.from_numpy(p2).to(dev)
+    out = _ops().moe_block(xb, lg_d, topk, p1d, p2d, SB)
+    ids, g = _ops().moe_router(lg_d, topk)
+    two = _ops().moe_grouped(xb, ids, g, p1d, p2d, SB)
+    torch.cuda.synchronize()
+    assert torch.equal(out, two)
+    ref_ids, ref_g = O.router(lg, topk)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    _check_close(out.cpu().numpy(), O.moe(x_bits, ref_ids, ref_g, list(p1), list(p2), SB),
+                 f"moe block t{t} e{e} top{topk}")
+
+
 def test_moe_deterministic(dev, experts):
     wl = I.WORKLOADS["moe_t1024_zipf"]
     ids, g = I.moe_routing(wl)
