@@ -20,6 +20,7 @@ STATUS_NAMES = {
     3: "TQ4_E_ALIGN",
     4: "TQ4_E_WORKSPACE",
     5: "TQ4_E_DEVICE",
+    6: "TQ4_E_TOO_LARGE",
 }
 
 # every symbol include/tq4.h declares, with (restype, argtypes)
@@ -52,6 +53,7 @@ SIGNATURES = {
     "tq4_moe_block": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _I32, _P, _I64, _P, _U32, _P, _P,
                                      _SZ, _P]),
     "tq4_linear_rotated": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
+    "tq4_linear_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _U32, _P, _P]),
     "tq4_moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
     "tq4_moe_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64]),
     "tq4_moe_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _P, _I64, _P, _U32,

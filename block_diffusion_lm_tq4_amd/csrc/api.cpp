@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/tq4.h"
 #include "tq4_internal.h"
 
@@ -93,6 +95,7 @@ const char *tq4_status_string(int status) {
     case TQ4_E_ALIGN: return "pointer misaligned";
     case TQ4_E_WORKSPACE: return "workspace missing or too small";
     case TQ4_E_DEVICE: return "HIP call or kernel launch failed";
+    case TQ4_E_TOO_LARGE: return "sizes need more scratch than the static scratch holds";
     default: return "unknown status";
   }
 }
@@ -153,9 +156,10 @@ size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n) {
 
 namespace {
 
-int linear_impl(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed, int64_t n,
-                uint32_t sign_bits, const tq4::Tail &tail, void *y, void *workspace,
-                size_t workspace_bytes, void *stream) {
+// Argument checks of the linear layer; none touches the device.  TQ4_OK means
+// the call may proceed (it is then a no-op if m or n is 0).
+int linear_args(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed, int64_t n,
+                const tq4::Tail &tail, const void *y) {
   if (m < 0 || k < 0 || n < 0 || k % 32 != 0) return TQ4_E_SHAPE;
   if (m == 0 || n == 0) return TQ4_OK;
   if (y == nullptr) return TQ4_E_NULL;
@@ -169,14 +173,24 @@ int linear_impl(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *pac
     const uintptr_t bytes = static_cast<uintptr_t>(m) * static_cast<uintptr_t>(n) * elem;
     if (r0 < y0 + bytes && y0 < r0 + bytes) return TQ4_E_SHAPE;
   }
+  if (k == 0) return TQ4_OK;
+  if (x_bf16 == nullptr || packed == nullptr) return TQ4_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(packed, 4)) return TQ4_E_ALIGN;
+  return TQ4_OK;
+}
+
+int linear_impl(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed, int64_t n,
+                uint32_t sign_bits, const tq4::Tail &tail, void *y, void *workspace,
+                size_t workspace_bytes, void *stream) {
+  const int st = linear_args(x_bf16, m, k, packed, n, tail, y);
+  if (st != TQ4_OK) return st;
+  if (m == 0 || n == 0) return TQ4_OK;
   hipStream_t s = as_stream(stream);
   float *yf = static_cast<float *>(y);  // bf16 outputs are addressed as such by the kernels
   const bool plain = tail.bias == nullptr && tail.residual == nullptr && !tail.bf16;
   if (k == 0)
     return device_status(plain ? tq4::launch_fill_zero(yf, m * n, s)
                                : tq4::launch_tail_only(tail, m, n, yf, s));
-  if (x_bf16 == nullptr || packed == nullptr) return TQ4_E_NULL;
-  if (!aligned(x_bf16, 16) || !aligned(packed, 4)) return TQ4_E_ALIGN;
   const LinearLayout l = linear_layout(m, k, n, false);
   const int ws_status = check_workspace(workspace, workspace_bytes, l.total);
   if (ws_status != TQ4_OK) return ws_status;
@@ -569,6 +583,56 @@ int tq4_moe_router(const float *logits, int64_t t, int32_t n_experts, int32_t to
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return TQ4_E_ALIGN;
   return device_status(
       tq4::launch_router(logits, t, n_experts, topk, topk_ids, topk_w, as_stream(stream)));
+}
+
+// ---- tq4_linear without a workspace argument -------------------------------
+// The scratch of tq4_linear (rotated activations and split-K partial sums)
+// lives in a device array of the library, one per GPU, so that the call
+// allocates nothing.  Host code never uses the array's name as an address:
+// its device address is looked up once per device and kept below.
+
+}  // extern "C"
+
+static __device__ __attribute__((aligned(256))) uint8_t scratch[TQ4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up on its first use; NULL if
+// the lookup fails.
+void *scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq4_linear_noalloc(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed,
+                       int64_t n, uint32_t sign_bits, float *y, void *stream) {
+  const int st = linear_args(x_bf16, m, k, packed, n, tq4::Tail{}, y);
+  if (st != TQ4_OK) return st;
+  if (m == 0 || n == 0) return TQ4_OK;
+  const size_t need = tq4_linear_workspace_size(m, k, n);
+  if (need > TQ4_NOALLOC_SCRATCH_BYTES) return TQ4_E_TOO_LARGE;
+  void *ws = nullptr;
+  if (need > 0) {
+    ws = scratch_for_current_device();
+    if (ws == nullptr) return TQ4_E_DEVICE;
+  }
+  return linear_impl(x_bf16, m, k, packed, n, sign_bits, tq4::Tail{}, y, ws,
+                     TQ4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

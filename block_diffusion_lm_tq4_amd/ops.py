@@ -257,6 +257,25 @@ def linear_fp8_quantized(x_codes: torch.Tensor, x_scales: torch.Tensor, k: int,
     return out
 
 
+def linear_noalloc(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """tq4_linear on the library's static scratch, no workspace (tq4_linear_noalloc)."""
+    _cuda_contig(x, "x", torch.bfloat16)
+    _cuda_contig(packed, "packed", torch.uint8)
+    m, k = x.shape
+    n = packed.shape[0]
+    _require(packed.dim() == 3 and packed.shape[1] * BLOCK == k and packed.shape[2] == BLOCK_BYTES,
+             "packed must be [n, k/32, 20]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _cuda_contig(out, "out", torch.float32)
+    _require(tuple(out.shape) == (m, n), "out must be [m, n]")
+    check("tq4_linear_noalloc", lib().tq4_linear_noalloc(
+        x.data_ptr(), m, k, packed.data_ptr(), n, sign_bits & 0xFFFFFFFF, out.data_ptr(),
+        _stream(x.device)))
+    return out
+
+
 def linear_rotated(xt: torch.Tensor, packed: torch.Tensor, out: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y = xt . Z_hat^T with xt = act_rht(x) already rotated (tq4_linear_rotated)."""

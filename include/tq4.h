@@ -73,7 +73,8 @@ typedef enum {
   TQ4_E_SHAPE = 2,       /* a size is out of range (k % 32 != 0, topk > E, ...) */
   TQ4_E_ALIGN = 3,       /* a pointer is not aligned as its argument requires   */
   TQ4_E_WORKSPACE = 4,   /* workspace NULL or smaller than the size query says  */
-  TQ4_E_DEVICE = 5       /* a HIP call or kernel launch failed                  */
+  TQ4_E_DEVICE = 5,      /* a HIP call or kernel launch failed                  */
+  TQ4_E_TOO_LARGE = 6    /* sizes need more than the static scratch holds       */
 } tq4_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -144,6 +145,29 @@ size_t tq4_linear_workspace_size(int64_t m, int64_t k, int64_t n);
 int tq4_linear(const uint16_t *x_bf16, int64_t m, int64_t k,
                const uint8_t *packed, int64_t n, uint32_t sign_bits, float *y,
                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of the library's static device scratch used by tq4_linear_noalloc
+ * (32 MiB; each GPU the library runs on holds one copy until the process
+ * ends). */
+#define TQ4_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* tq4_linear for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * result equals tq4_linear's bit for bit; the scratch that tq4_linear takes
+ * as its workspace is instead a device array inside the library (one per GPU,
+ * TQ4_NOALLOC_SCRATCH_BYTES), so the call allocates and frees nothing.  The
+ * array's device address is looked up on the first call on each device.
+ *   arguments as tq4_linear, without the workspace
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (no call relies on them): calls that may overlap on one GPU (other
+ * streams, other host threads) race and must be serialized by the caller.
+ * Errors: as tq4_linear, plus TQ4_E_TOO_LARGE when
+ * tq4_linear_workspace_size(m, k, n) exceeds TQ4_NOALLOC_SCRATCH_BYTES (for
+ * example m * k above about 16.7 M rotated activations), and TQ4_E_DEVICE if
+ * the array's address cannot be looked up. */
+int tq4_linear_noalloc(const uint16_t *x_bf16, int64_t m, int64_t k,
+                       const uint8_t *packed, int64_t n, uint32_t sign_bits, float *y,
+                       void *stream);
 
 /* The same product with the activations already rotated: y = xt . Z_hat^T,
  * where xt = tq4_act_rht(x) (fp16 bit patterns [m, k], device, 16-byte

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    for s in range(6):
+    for s in range(7):
         assert L.tq4_status_string(s)
     assert L.tq4_status_string(99) == b"unknown status"
     assert L.tq4_version() >= 100
@@ -114,6 +114,33 @@ def test_linear_argument_errors(L):
     assert call(wsb=ws - 1) == E_WS
     assert call(ws=FAKE + 16) == E_ALIGN
     assert call(m=0) == OK and call(n=0) == OK      # empty output: no-op
+
+
+def test_linear_noalloc_argument_errors(L):
+    """tq4_linear_noalloc rejects bad arguments and sizes beyond its static
+    scratch before any device call (these run without a GPU)."""
+    E_TOO_LARGE = 6
+    assert L.tq4_status_string(E_TOO_LARGE) != b"unknown status"
+    args = dict(x=FAKE, m=100, k=2688, p=FAKE, n=8192, sb=0, y=FAKE)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.tq4_linear_noalloc(a["x"], a["m"], a["k"], a["p"], a["n"], a["sb"], a["y"],
+                                    None)
+
+    assert call(k=2690) == E_SHAPE
+    assert call(m=-1) == E_SHAPE
+    assert call(x=None) == E_NULL
+    assert call(p=None) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(x=MIS) == E_ALIGN
+    assert call(y=FAKE + 2) == E_ALIGN
+    assert call(m=0) == OK and call(n=0) == OK      # empty output: no-op
+    # 8192 x 4096 rotated activations alone are 64 MiB, beyond the 32 MiB scratch
+    assert L.tq4_linear_workspace_size(8192, 4096, 64) > (32 << 20)
+    assert call(m=8192, k=4096, n=64) == E_TOO_LARGE
+    # M=4096 at K=2688 (256 x 256 tiles, no split) fits
+    assert L.tq4_linear_workspace_size(4096, 2688, 8192) <= (32 << 20)
 
 
 def test_linear_epilogue_argument_errors(L):
