@@ -5,8 +5,9 @@ Headline (`value`): packed-weight GB/s of one dense denoiser-step projection,
 M=16 tokens (one 16-token diffusion block), K=2688, N=8192, through
 tq4_linear (activation rotation + dequant-GEMM).  A step is one such call;
 the weights rotate over `--copies` distinct packed copies (48 x 13.76 MB =
-660 MB, more than twice the 256 MB Infinity Cache), so every step streams
-its weights from HBM.  Inputs are resident in HBM before timing starts.
+660 MB, more than twice the 256 MB Infinity Cache), and the cache is flushed
+before the timed steps, so every step streams its weights from HBM whatever
+the step count.  Inputs are resident in HBM before timing starts.
 
 Extra legs in the same JSON line: the M=4096 prefill projection (TFLOP/s,
 Student-t weights) and the 128-expert top-6 MoE layer at 16 and 1024 tokens
@@ -67,15 +68,33 @@ def load_traffic(key: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+_FLUSH = {}
+
+
+def mall_flush(torch):
+    """Read a 512 MiB buffer (twice the 256 MB Infinity Cache), so that no
+    input of the next timed region is still cached from an earlier call.  A
+    read leaves clean lines only: writing the buffer instead would leave
+    dirty lines whose write-back would land inside the timed region."""
+    from block_diffusion_lm_tq4_amd import ops
+    if "buf" not in _FLUSH:
+        _FLUSH["buf"] = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+        _FLUSH["sink"] = torch.zeros(256, dtype=torch.float32, device="cuda")
+        ops.read_probe(_FLUSH["buf"], _FLUSH["sink"])  # the zero fill's lines, written back
+    ops.read_probe(_FLUSH["buf"], _FLUSH["sink"])
+
+
 def time_loop(torch, fn, steps: int, warmup: int) -> float:
     """Average ms per call of fn(i) over exactly `steps` calls.
 
     The calls are captured once into a HIP graph (the library launches on
     torch's current stream, which is the capture stream) and the graph is
     replayed, so the GPU runs them back to back without host launch overhead.
-    `warmup` eager calls and one untimed replay come first.  HIP events on the
-    replay stream bracket the timed replay, with device synchronization on
-    both sides.
+    `warmup` eager calls and one untimed replay come first; then a 512 MiB
+    write evicts the Infinity Cache, so the timed replay reads every input
+    that the graph's calls do not share from HBM, whatever the step count.
+    HIP events on the replay stream bracket the timed replay, with device
+    synchronization on both sides.
     """
     for i in range(warmup):
         fn(i)
@@ -85,6 +104,7 @@ def time_loop(torch, fn, steps: int, warmup: int) -> float:
         for i in range(steps):
             fn(i)
     graph.replay()
+    mall_flush(torch)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -304,30 +324,131 @@ def pack_leg(torch, np, ops, I, steps, warmup, dev, sb, n=8192, k=2688):
 
 # ----------------------------------------------------------------------- CPU side
 
-def cpu_baseline(np, I, budget_s: float = 12.0):
-    """The fp64 oracle on a bounded slice of the M=16 workload, all host threads."""
-    import oracle as O
+CPU_BLAS_ENV = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+
+
+def cpu_host():
+    """CPU model, logical CPU count and the CPUs this process may run on."""
+    model = None
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    rows = 1024
-    w = I.weights(rows, 2688)
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "os_cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
+
+
+def cpu_units(budget_s: float):
+    """The fp64 oracle on bounded samples of each workload's unit of work,
+    each sample repeated for about budget_s seconds in this process.  Returns
+    {unit: {"work": amount per second, "unit", "calls", "seconds", "sample"}}."""
+    import numpy as np
+
+    import oracle as O
+    from block_diffusion_lm_tq4_amd import inputs as I
+
     sb = I.sign_bits()
-    packed = O.pack(w, sb)
-    x = I.activations_bf16(16, 2688)
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        O.linear(x, packed, sb)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    gbs = packed.nbytes * calls / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"dense M=16 K=2688 projection, {rows} of 8192 weight rows "
-                      f"(unpack + rotate + fp64 matmul), {calls} calls in {el:.1f} s"}
+    units = {}
+
+    def timed(name, fn, work, unit, sample):
+        fn()  # first call outside the clock (page faults, BLAS start-up)
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+        units[name] = {"work": work * calls / el, "unit": unit, "calls": calls,
+                       "seconds": round(el, 2), "sample": sample}
+
+    # dense M=16: 1024 of the 8192 weight rows; unit = packed bytes
+    p16 = O.pack(I.weights(1024, 2688), sb)
+    x16 = I.activations_bf16(16, 2688)
+    timed("dense_m16", lambda: O.linear(x16, p16, sb), p16.nbytes, "B/s",
+          "M=16, K=2688, 1024 of 8192 weight rows: unpack + rotate + fp64 matmul")
+    # dense M=4096 (Student-t weights): all 4096 tokens against 64 weight rows
+    p4k = O.pack(I.weights(64, 2688, "student_t3"), sb)
+    x4k = I.activations_bf16(4096, 2688)
+    timed("dense_m4096_t3", lambda: O.linear(x4k, p4k, sb), 2.0 * 4096 * 64 * 2688, "FLOP/s",
+          "M=4096, K=2688, 64 of 8192 weight rows")
+    # MoE, 16 tokens: the layer restricted to one expert that every token
+    # routes to (top-1, gate 1); unit = that expert's packed bytes
+    e_up = O.pack(I.expert_weights(0, 1), sb)
+    e_dn = O.pack(I.expert_weights(0, 2), sb)
+    xm = I.activations_bf16(16, 2688)
+    ids = np.zeros((16, 1), dtype=np.int32)
+    g = np.ones((16, 1), dtype=np.float32)
+    timed("moe_t16", lambda: O.moe(xm, ids, g, [e_up], [e_dn], sb),
+          e_up.nbytes + e_dn.nbytes, "B/s",
+          "16 tokens through one 1856x2688 / 2688x1856 expert (both projections)")
+    # the encoder: 256 rows of the dense projection; unit = weights
+    wp = I.weights(256, 2688)
+    timed("pack", lambda: O.pack(wp, sb), wp.size, "weights/s", "256 x 2688 fp32 weights")
+    return units
+
+
+def _cpu_worker(budget_s):
+    return cpu_units(budget_s)
+
+
+def cpu_leg_main(kind: str, workers: int, budget_s: float) -> int:
+    """Entry of the child process that times the oracle (no GPU use here)."""
+    if kind == "single":
+        res = cpu_units(budget_s)
+    else:
+        from concurrent.futures import ProcessPoolExecutor
+        with ProcessPoolExecutor(workers) as ex:
+            parts = list(ex.map(_cpu_worker, [budget_s] * workers))
+        res = {}
+        for name in parts[0]:
+            res[name] = dict(parts[0][name])
+            res[name]["work"] = sum(p[name]["work"] for p in parts)
+            res[name]["calls"] = sum(p[name]["calls"] for p in parts)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline(budget_s: float = 2.5):
+    """The fp64 oracle timed on this host, single-threaded and on all cores.
+
+    Each leg runs in a child process that never touches the GPU, with the
+    BLAS thread count fixed through the environment: single-threaded (one
+    process, one BLAS thread) and all-core (one single-threaded process per
+    available CPU, up to 16, each running the same samples; the samples are
+    independent row or expert slices, so their rates add)."""
+    import subprocess
+    host = cpu_host()
+    workers = max(1, min(host["affinity"], 16))
+    legs = {}
+    for kind, n in (("single", 1), ("all", workers)):
+        env = dict(os.environ)
+        for v in CPU_BLAS_ENV:
+            env[v] = "1"
+        cmd = [sys.executable, os.path.abspath(__file__), "--cpu-leg", kind,
+               "--cpu-workers", str(n), "--cpu-budget", str(budget_s)]
+        res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+        if res.returncode != 0:
+            raise RuntimeError(f"cpu leg {kind} failed: {res.stderr[-2000:]}")
+        legs[kind] = json.loads(res.stdout.strip().splitlines()[-1])
+
+    def fmt(u):
+        scale = {"B/s": (1e-9, "GB/s"), "FLOP/s": (1e-9, "GFLOP/s"),
+                 "weights/s": (1e-6, "Mweights/s")}[u["unit"]]
+        return {"value": float(f"{u['work'] * scale[0]:.4g}"), "unit": scale[1],
+                "calls": u["calls"], "seconds": u["seconds"], "sample": u["sample"]}
+
+    single = {k: fmt(v) for k, v in legs["single"].items()}
+    allc = {k: fmt(v) for k, v in legs["all"].items()}
+    return {"value": allc["dense_m16"]["value"], "unit": "GB/s", "cores": workers,
+            "kind": "oracle",
+            "sample": "dense M=16 K=2688 projection, 1024 of 8192 weight rows (unpack + "
+                      f"rotate + fp64 matmul), {workers} single-threaded processes",
+            "host": host, "single_thread": single, "all_core": allc}
 
 
 # ---------------------------------------------------------------------------- main
@@ -339,15 +460,22 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=48)
     ap.add_argument("--legs", default="all",
-                    help="all | none | comma list of dense_m4096_t3,moe_t16,"
+                    help="all | none | comma list of linear_512x256,dense_m4096_t3,moe_t16,"
                          "moe_t1024_uniform,moe_t1024_zipf,pack,epilogue,fp8")
     ap.add_argument("--only", default=None,
                     help="profile helper: run just this workload (no JSON contract)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-leg", choices=("single", "all"), default=None,
+                    help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-workers", type=int, default=1, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-budget", type=float, default=2.5, help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: also run a plain 512 MiB device copy three times, "
                          "the reference for scaling HBM byte counters")
     args = ap.parse_args()
+
+    if args.cpu_leg:
+        return cpu_leg_main(args.cpu_leg, args.cpu_workers, args.cpu_budget)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -412,8 +540,8 @@ def main() -> int:
 
     legs = {}
     names = ([] if args.legs == "none" else
-             ["dense_m4096_t3", "moe_t16", "moe_t1024_uniform", "moe_t1024_zipf", "pack",
-              "epilogue", "fp8"]
+             ["linear_512x256", "dense_m4096_t3", "moe_t16", "moe_t1024_uniform",
+              "moe_t1024_zipf", "pack", "epilogue", "fp8"]
              if args.legs == "all" else args.legs.split(","))
     experts = fp8_experts = None
     for name in names:
@@ -473,6 +601,18 @@ def main() -> int:
             log(name, json.dumps(legs[name]))
             continue
         wl2 = I.WORKLOADS[name]
+        if name == "linear_512x256":
+            # the small parity layer: latency-bound, reported in microseconds
+            log(f"{name}: running")
+            q = dense_leg(torch, np, ops, I, wl2, max(5, args.steps // 2),
+                          max(2, args.warmup // 2), args.copies, dev, sb)
+            legs[name] = {"us_per_call": round(q["ms_step"] * 1e3, 3),
+                          "plain_read_us": round(q["ms_read"] * 1e3, 3),
+                          "packed_bytes": q["packed_bytes"],
+                          "shape": f"M={wl2.m} K={wl2.k} N={wl2.n}",
+                          "note": "no roofline target: 81,920 packed bytes per call"}
+            log(name, json.dumps(legs[name]))
+            continue
         if name.startswith("dense"):
             log(f"{name}: running")
             s2 = max(5, args.steps // 20)
@@ -523,7 +663,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu_baseline: timing the fp64 oracle")
-        cpu = cpu_baseline(np, I)
+        cpu = cpu_baseline()
 
     line = {
         "metric": "packed-weight GB/s & TFLOP/s of TQ4_1S dequant-GEMM at M=16 and M=4096",
@@ -541,7 +681,9 @@ def main() -> int:
         "config": {"workload": "dense_m16: TQ4_1S linear, M=16 tokens, K=2688, N=8192, "
                                "W~N(0,0.02^2) packed, x bf16~N(0,1), "
                                f"{args.copies} rotating weight copies",
-                   "global_batch": wl.m, "parallelism": "none (1 GPU)"},
+                   "global_batch": wl.m, "parallelism": "none (1 GPU)",
+                   "weight_copies_read_in_timed_steps": min(args.steps, args.copies),
+                   "infinity_cache_flushed_before_timing": True},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "legs": legs,
