@@ -10,7 +10,10 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq4.so")
+# TQ4_LIBRARY selects another build of the same library (for example the
+# sanitizer build of block_diffusion_lm_tq4_amd.build.build_sanitized)
+LIB_PATH = os.environ.get("TQ4_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libtq4.so")
 
 TQ4_OK = 0
 STATUS_NAMES = {

@@ -94,5 +94,70 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+SANITIZED_DIR = os.path.join(BUILD, "sanitized")
+SANITIZED_LIB = os.path.join(SANITIZED_DIR, "libtq4.so")
+# host-only sanitizers: each flag applies to the host pass of hipcc only, so
+# device code is compiled exactly as in the normal build
+_HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                  "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libtq4.so with the host-side C-ABI layer (api.cpp, codebook.cpp) built
+    under AddressSanitizer and UndefinedBehaviorSanitizer, the kernels as in
+    the normal build; for running the ABI tests under the sanitizers (load it
+    through TQ4_LIBRARY with the sanitizer runtime preloaded)."""
+    hipcc = _hipcc()
+    os.makedirs(SANITIZED_DIR, exist_ok=True)
+    objs = []
+    for src, extra in SOURCES.items():
+        obj = os.path.join(SANITIZED_DIR, src + ".o")
+        cmd = [hipcc, *_common_flags(), *extra]
+        if src.endswith(".cpp"):
+            cmd = [hipcc, "-x", "hip", *_common_flags(), *extra, *_HOST_SANITIZE]
+        cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+        objs.append(obj)
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc)), "..", "lib", "llvm", "bin",
+                         "clang++")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang++"
+    cmd = [clang, "-shared", "-fPIC", "-fsanitize=address", "-fsanitize=undefined",
+           "-shared-libsan", "-o", SANITIZED_LIB, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,/opt/rocm/lib"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    if verbose:
+        print(f"built {SANITIZED_LIB}", file=sys.stderr)
+    return SANITIZED_LIB
+
+
+TEST_NATIVE = os.path.join(ROOT, "tests", "native")
+
+
+def build_test_probes(verbose: bool = False) -> list[str]:
+    """Compile the test-only kernels under tests/native/ (one shared library
+    each, next to its source); returns their paths."""
+    hipcc = _hipcc()
+    out = []
+    for src in sorted(os.listdir(TEST_NATIVE)) if os.path.isdir(TEST_NATIVE) else []:
+        if not src.endswith(".hip"):
+            continue
+        lib = os.path.join(TEST_NATIVE, "lib" + src[:-4] + ".so")
+        cmd = [hipcc, *_common_flags(), "-shared", os.path.join(TEST_NATIVE, src), "-o", lib]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+        if verbose:
+            print(f"built {lib}", file=sys.stderr)
+        out.append(lib)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose="--verbose" in sys.argv)
+    build_test_probes(verbose="--verbose" in sys.argv)

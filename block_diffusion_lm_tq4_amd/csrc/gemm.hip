@@ -283,6 +283,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
   auto issue_a = [&](int c, uint8_t *buf) {
 #pragma unroll
     for (int i = 0; i < MSUB; ++i) {
+      // MoE: 4-row groups past the tile's rows are not loaded; their LDS rows
+      // keep earlier values, which reach only outputs that are not stored
+      if (MODE != kDense && i + wave > 0 && 4 * (wave * MSUB + i) >= rows_valid) break;
       const int blk = 4 * c + aslot[i] / 4;
       const uint16_t *src = asrc[i] + (blk < kb ? 128 * c + 8 * aslot[i] : 0);
       __builtin_amdgcn_global_load_lds((const global_void *)src,
@@ -340,6 +343,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
       const int slot = (4 * grp + t) ^ r;
 #pragma unroll
       for (int i = 0; i < MSUB; ++i) {
+        // an MoE tile holds as many rows as its expert has left: 16-row
+        // sub-tiles past them (uniform per workgroup) are skipped
+        if (MODE != kDense && i > 0 && 16 * i >= rows_valid) break;
         const half8 aq =
             *reinterpret_cast<const half8 *>(abase + (16 * i + r) * kChunkBytes + 16 * slot);
 #pragma unroll

@@ -41,6 +41,48 @@ constexpr float kSkinnyUnscale = 0x1.6a09e6p-8f;
 // bf16 bits of +-2^-3, the entries of the M <= 16 kernels' rotation operand
 constexpr uint16_t kRotEntryBF16 = 0x3E00u;
 
+// Register decode of the codebook (no memory access): the 16 levels are
+// symmetric, c_{15-j} = -c_j, so the fp16 bit patterns of the 8 positive
+// levels c_8 .. c_15 fit in four 32-bit byte tables (low bytes of levels
+// 0-3 and 4-7, high bytes of levels 0-3 and 4-7), and v_perm_b32 turns four
+// 3-bit magnitude indices into four table bytes at once.  A code q >= 8 is
+// +level q - 8; q < 8 is -level 7 - q, i.e. magnitude index q ^ 7 with the
+// sign bit set.
+struct PermTable {
+  uint32_t lo03, lo47, hi03, hi47;
+};
+
+__device__ inline PermTable make_perm_table(const Codebook &cb) {
+  uint32_t b[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(cb.c[8 + j]));
+  PermTable t;
+  t.lo03 = (b[0] & 0xFFu) | (b[1] & 0xFFu) << 8 | (b[2] & 0xFFu) << 16 | (b[3] & 0xFFu) << 24;
+  t.lo47 = (b[4] & 0xFFu) | (b[5] & 0xFFu) << 8 | (b[6] & 0xFFu) << 16 | (b[7] & 0xFFu) << 24;
+  t.hi03 = (b[0] >> 8) | (b[1] >> 8) << 8 | (b[2] >> 8) << 16 | (b[3] >> 8) << 24;
+  t.hi47 = (b[4] >> 8) | (b[5] >> 8) << 8 | (b[6] >> 8) << 16 | (b[7] >> 8) << 24;
+  return t;
+}
+
+// The 8 fp16 levels of one code word (nibble i = code of element i), as four
+// packed pairs in the order of elements (0,2), (4,6), (1,3), (5,7): each
+// pair is the low and high byte of two table lookups, merged by one
+// v_perm_b32.  Callers pair them with activations in that element order.
+__device__ inline void decode8_perm(uint32_t w, const PermTable &t, uint32_t (&d)[4]) {
+  const uint32_t neg = ~w & 0x88888888u;            // bit 3 of every code below 8
+  const uint32_t j = w ^ (neg - (neg >> 3));        // magnitude index in bits 0-2
+  const uint32_t ev = j & 0x07070707u;              // elements 0, 2, 4, 6
+  const uint32_t od = (j >> 4) & 0x07070707u;       // elements 1, 3, 5, 7
+  const uint32_t ev_lo = __builtin_amdgcn_perm(t.lo47, t.lo03, ev);
+  const uint32_t ev_hi = __builtin_amdgcn_perm(t.hi47, t.hi03, ev) | ((neg << 4) & 0x80808080u);
+  const uint32_t od_lo = __builtin_amdgcn_perm(t.lo47, t.lo03, od);
+  const uint32_t od_hi = __builtin_amdgcn_perm(t.hi47, t.hi03, od) | (neg & 0x80808080u);
+  d[0] = __builtin_amdgcn_perm(ev_hi, ev_lo, 0x05010400u);  // elements 0, 2
+  d[1] = __builtin_amdgcn_perm(ev_hi, ev_lo, 0x07030602u);  // elements 4, 6
+  d[2] = __builtin_amdgcn_perm(od_hi, od_lo, 0x05010400u);  // elements 1, 3
+  d[3] = __builtin_amdgcn_perm(od_hi, od_lo, 0x07030602u);  // elements 5, 7
+}
+
 // xt = H32 diag(s) x / sqrt(32) of one 32-element block: bf16 in (16-byte
 // aligned), fp32 butterfly in natural (Sylvester) order, fp16 out.  The format
 // rotates every weight block by this orthogonal matrix (Nemotron-TheHobbit-

@@ -3,10 +3,11 @@
 Codes and scale bytes are compared bit for bit (both sides decide them in
 fp64, or from exactly scaled fp32 values for the activations).  The product is
 compared with the oracle's fp64 product of the same fp8 operands.  The
-block-scaled fp8 MFMA does not sum a 32-block's products exactly: measured on
-the device, it keeps each product to a window of 13 bits below the block's
-largest product (a product 2^-14 of the largest one is dropped, one 2^-13 of
-it is kept), while block sums and the running sum are combined in fp32.  So
+block-scaled fp8 MFMA need not sum a 32-block's products exactly: a product
+at least 2^-13 of the block's largest is summed exactly and a smaller one errs
+by less than 2^-13 of the largest, while block sums and the running sum are
+combined in fp32; tests/test_gpu_fp8_window.py checks exactly this on the
+device.  So
 each element must lie within
     31 * 2^-13 * sum_b max_k|x| max_k|w|   (over the 32-blocks b, k in b)
   + (2 * steps + 8) * 2^-24 * sum_k |x_k w_k|

@@ -29,6 +29,7 @@ import torch
 
 import oracle as O
 from block_diffusion_lm_tq4_amd import inputs as I
+from fp8_bracket import check_bracket as _check_bracket
 
 pytestmark = pytest.mark.gpu
 
@@ -50,80 +51,6 @@ def _ops():
 
 def _bf16(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-
-def _kp(k):
-    return (k + 127) // 128 * 128
-
-
-def _mfma_bound(ad, bd, kp):
-    """Bound on |device - exact| for ad . bd^T on the block-scaled fp8 MFMA."""
-    k = ad.shape[1]
-    aa = np.max(np.abs(ad).reshape(ad.shape[0], k // 32, 32), axis=-1)
-    bb = np.max(np.abs(bd).reshape(bd.shape[0], k // 32, 32), axis=-1)
-    return (31 * 2.0 ** -13 * (aa @ bb.T)
-            + (2 * (kp // 128) + 8) * 2.0 ** -24 * (np.abs(ad) @ np.abs(bd).T))
-
-
-def _quantized_range(h_lo, h_hi):
-    """[d_min, d_max] of the MXFP8 values the device may store for hidden
-    values in [h_lo, h_hi] (per element, rows x n1)."""
-    rows, n1 = h_lo.shape
-    blo = h_lo.reshape(rows, n1 // 32, 32)
-    bhi = h_hi.reshape(rows, n1 // 32, 32)
-    e_lo = O.e8m0_exponent(blo.max(-1))
-    e_hi = O.e8m0_exponent(bhi.max(-1))
-    assert np.all(e_hi - e_lo <= 1), "error bound too wide to enumerate exponents"
-    vals = O.e4m3_values()
-    d_min = np.full(blo.shape, np.inf)
-    d_max = np.full(blo.shape, -np.inf)
-    for c in (0, 1):
-        e = (e_lo + c)[..., None]
-        ok = np.broadcast_to(e <= e_hi[..., None], blo.shape)
-        cap = np.ldexp(448.0, e)
-        for src, dst, pick in ((blo, d_min, np.minimum), (bhi, d_max, np.maximum)):
-            scaled = np.where(ok, np.ldexp(np.minimum(src, cap), -e), 0.0)
-            q = np.ldexp(vals[O.e4m3_round(scaled)], e)
-            dst[...] = np.where(ok, pick(dst, q), dst)
-    return d_min.reshape(rows, n1), d_max.reshape(rows, n1)
-
-
-def _check_bracket(out, x, ids, g, c1, c2, tokens, what):
-    """Every out[tokens] element lies in the interval the oracle derives."""
-    xd = O.mx_dequant(*O.act_mxfp8(x))[tokens]
-    sel = ids[tokens]
-    gsel = g[tokens].astype(np.float64)
-    topk = ids.shape[1]
-    k = x.shape[1]
-    centre = np.zeros((len(tokens), k))
-    radius = np.zeros((len(tokens), k))
-    for e in np.unique(sel):
-        if e < 0 or e >= len(c1):
-            continue
-        rows, js = np.nonzero(sel == e)
-        w1 = O.mx_dequant(*c1[int(e)])
-        w2 = O.mx_dequant(*c2[int(e)])
-        a = xd[rows]
-        u = a @ w1.T
-        b1 = _mfma_bound(a, w1, _kp(k)) * (1 + 1e-9) + 1e-30
-        h_lo = np.maximum(u - b1, 0.0) ** 2 * (1 - 2.0 ** -22)
-        h_hi = np.maximum(u + b1, 0.0) ** 2 * (1 + 2.0 ** -22) + 2.0 ** -140
-        d_min, d_max = _quantized_range(h_lo, h_hi)
-        mid, rad = (d_min + d_max) / 2, (d_max - d_min) / 2
-        mag = np.maximum(np.abs(d_min), np.abs(d_max))
-        o_c = mid @ w2.T
-        o_r = rad @ np.abs(w2).T + _mfma_bound(mag, w2, _kp(w2.shape[1])) * (1 + 1e-9)
-        gj = gsel[rows, js][:, None]
-        np.add.at(centre, rows, gj * o_c)
-        np.add.at(radius, rows, np.abs(gj) * (o_r + (topk + 1) * 2.0 ** -24 * (np.abs(o_c) + o_r)))
-    y = np.asarray(out, np.float64)[tokens]
-    err = np.abs(y - centre)
-    ratio = np.max(err / np.maximum(radius, 1e-300))
-    ref = O.moe_fp8(x, ids, g, c1, c2, tokens=tokens)
-    relf = np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300)
-    print(f"{what}: max err / bracket = {ratio:.3e}, relF to the oracle {relf:.2e}")
-    assert np.all(err <= radius + 1e-30), what
-    assert relf <= 2e-2, (what, relf)
 
 
 class _Experts:
