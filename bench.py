@@ -304,6 +304,39 @@ def fp8_leg(torch, np, ops, I, wl, steps, warmup, copies, dev, sb):
     return r
 
 
+def rotation_ab_leg(torch, np, ops, I, steps, warmup, copies, dev, sb):
+    """The rotation placement and the product arithmetic, measured
+    (tq4_linear_variant): at M=16 the library's product (activation rotation,
+    MFMA), the rotation undone on the weight tiles (MFMA products), and the
+    products on the VALU; at M=4096 the two placements."""
+    out = {}
+    for name, variants, cps, st, wu in (
+            ("dense_m16", ("default", "weight_rotation", "valu_product"), copies, steps, warmup),
+            ("dense_m4096_t3", ("default", "weight_rotation"), 2, max(5, steps // 20),
+             max(2, warmup // 10))):
+        wl = I.WORKLOADS[name]
+        w = I.weights(wl.n, wl.k, wl.weights)
+        packed = ops.pack(torch.from_numpy(w).to(dev), sb)
+        del w
+        stack = [packed] + [packed.clone() for _ in range(cps - 1)]
+        x = bf16_dev(torch, np, I.activations_bf16(wl.m, wl.k), dev)
+        y = torch.empty((wl.m, wl.n), dtype=torch.float32, device=dev)
+        ws = torch.zeros(max(ops.linear_workspace_size(wl.m, wl.k, wl.n), wl.m * wl.k * 2),
+                         dtype=torch.uint8, device=dev)
+        leg = {}
+        for v in variants:
+            ms = time_loop(torch, lambda i, v=v: ops.linear_variant(
+                x, stack[i % cps], sb, v, out=y, workspace=ws), st, wu)
+            leg[v] = {"us": round(ms * 1e3, 2)}
+            if wl.m <= 16:
+                leg[v]["GB/s"] = round(packed.numel() / (ms * 1e-3) / 1e9, 1)
+            else:
+                leg[v]["TFLOP/s"] = round(2.0 * wl.m * wl.n * wl.k / (ms * 1e-3) / 1e12, 1)
+        out[name] = leg
+        del stack, packed
+    return out
+
+
 def pack_leg(torch, np, ops, I, steps, warmup, dev, sb, n=8192, k=2688):
     """Offline quantizer throughput (tq4_pack_bf16 and tq4_pack) on one
     denoiser-projection-sized matrix, weights resident on the device."""
@@ -461,6 +494,7 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=48)
     ap.add_argument("--legs", default="all",
                     help="all | none | comma list of linear_512x256,dense_m4096_t3,moe_t16,"
+                         "rotation_ab,"
                          "moe_t1024_uniform,moe_t1024_zipf,pack,epilogue,fp8")
     ap.add_argument("--only", default=None,
                     help="profile helper: run just this workload (no JSON contract)")
@@ -496,6 +530,10 @@ def main() -> int:
     sb = I.sign_bits()
 
     if args.only:
+        if args.only == "rotation_ab":
+            r = rotation_ab_leg(torch, np, ops, I, args.steps, args.warmup, args.copies, dev, sb)
+            log(args.only, json.dumps(r))
+            return 0
         if args.only.startswith("fp8_"):
             wl = I.WORKLOADS[args.only[4:]]
             r = fp8_leg(torch, np, ops, I, wl, args.steps, args.warmup,
@@ -541,7 +579,7 @@ def main() -> int:
     legs = {}
     names = ([] if args.legs == "none" else
              ["linear_512x256", "dense_m4096_t3", "moe_t16", "moe_t1024_uniform",
-              "moe_t1024_zipf", "pack", "epilogue", "fp8"]
+              "moe_t1024_zipf", "pack", "epilogue", "fp8", "rotation_ab"]
              if args.legs == "all" else args.legs.split(","))
     experts = fp8_experts = None
     for name in names:
@@ -588,6 +626,12 @@ def main() -> int:
                 leg["dense_m4096_t3"]["context_fp8_blas"] = {"error": q4k["fp8_blas_error"]}
             legs[name] = leg
             log(name, json.dumps(leg))
+            continue
+        if name == "rotation_ab":
+            log("rotation_ab: running")
+            legs[name] = rotation_ab_leg(torch, np, ops, I, max(5, args.steps // 2),
+                                         max(2, args.warmup // 2), args.copies, dev, sb)
+            log(name, json.dumps(legs[name]))
             continue
         if name == "epilogue":
             log("epilogue: running")

@@ -57,6 +57,8 @@ SIGNATURES = {
                                      _SZ, _P]),
     "tq4_linear_rotated": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "tq4_linear_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _U32, _P, _P]),
+    "tq4_linear_variant": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _U32, _P, _P, _SZ,
+                                          ctypes.c_int, _P]),
     "tq4_moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
     "tq4_moe_workspace_size": (_SZ, [_I64, _I32, _I32, _I64, _I64]),
     "tq4_moe_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I32, _I32, _P, _I64, _P, _U32,

@@ -230,6 +230,33 @@ int tq4_linear_epilogue_bf16(const uint16_t *x_bf16, int64_t m, int64_t k, const
                      y_bf16, workspace, workspace_bytes, stream);
 }
 
+int tq4_linear_variant(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed,
+                       int64_t n, uint32_t sign_bits, float *y, void *workspace,
+                       size_t workspace_bytes, int variant, void *stream) {
+  if (variant == TQ4_VARIANT_DEFAULT)
+    return linear_impl(x_bf16, m, k, packed, n, sign_bits, tq4::Tail{}, y, workspace,
+                       workspace_bytes, stream);
+  if (variant != TQ4_VARIANT_WEIGHT_ROTATION && variant != TQ4_VARIANT_VALU_PRODUCT)
+    return TQ4_E_SHAPE;
+  const int st = linear_args(x_bf16, m, k, packed, n, tq4::Tail{}, y);
+  if (st != TQ4_OK) return st;
+  if (m == 0 || n == 0) return TQ4_OK;
+  if (k == 0) return TQ4_E_SHAPE;
+  hipStream_t s = as_stream(stream);
+  if (tq4::skinny_dma_fits(m, k, n, x_bf16, packed))
+    return device_status(tq4::launch_skinny_variant(
+        variant == TQ4_VARIANT_WEIGHT_ROTATION ? 1 : 2, x_bf16, m, k, packed, n, sign_bits, y, s));
+  if (variant != TQ4_VARIANT_WEIGHT_ROTATION || m <= 16 || !tq4::dense_huge_fits(m, k, n))
+    return TQ4_E_SHAPE;
+  const size_t need = static_cast<size_t>(m) * static_cast<size_t>(k) * 2;
+  const int ws_status = check_workspace(workspace, workspace_bytes, need);
+  if (ws_status != TQ4_OK) return ws_status;
+  uint16_t *xs = static_cast<uint16_t *>(workspace);
+  hipError_t e = tq4::launch_act_sign_f16(x_bf16, m, k, sign_bits, xs, s);
+  if (e == hipSuccess) e = tq4::launch_dense_weight_side(xs, m, k, packed, n, y, s);
+  return device_status(e);
+}
+
 int tq4_linear_rotated(const uint16_t *xt_f16, int64_t m, int64_t k, const uint8_t *packed,
                        int64_t n, float *y, void *workspace, size_t workspace_bytes,
                        void *stream) {

@@ -102,7 +102,7 @@ __device__ inline half8 dequant8(uint32_t codes, half2v scale, const uint32_t *l
 template <bool kCheck, bool kBF16, int MS, int NS>
 __device__ inline void store_tiles_impl(const floatx4 (&acc)[MS][NS], float *out, const Tail &t,
                                         int64_t m0, int64_t n0, int64_t mlim, int64_t nlim,
-                                        int grp, int r) {
+                                        int grp, int r, float unscale) {
   // Loads use indices clamped into the output, so they need no branches;
   // what they read for an element outside it is never stored.
   const auto clamp_m = [&](int64_t m) { return kCheck && m >= mlim ? mlim - 1 : m; };
@@ -135,9 +135,9 @@ __device__ inline void store_tiles_impl(const floatx4 (&acc)[MS][NS], float *out
       for (int j = 0; j < NS; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          // the weight shift undone (exact), then the same two adds, in
-          // order, as tail_sum
-          float a = acc[i0 + ii][j][v] * kWeightUnscale;
+          // the weight shift undone (exact for the library's products),
+          // then the same two adds, in order, as tail_sum
+          float a = acc[i0 + ii][j][v] * unscale;
           if (t.bias != nullptr) a += bv[j];
           if (t.residual != nullptr) a += y[ii][j][v];
           y[ii][j][v] = a;
@@ -162,18 +162,18 @@ __device__ inline void store_tiles_impl(const floatx4 (&acc)[MS][NS], float *out
 template <int MS, int NS>
 __device__ inline void store_tiles(const floatx4 (&acc)[MS][NS], float *out, const Tail &t,
                                    int64_t m0, int64_t n0, int64_t mlim, int64_t nlim, int grp,
-                                   int r) {
+                                   int r, float unscale = kWeightUnscale) {
   const bool full = m0 + 16 * MS <= mlim && n0 + 16 * NS <= nlim;
   if (t.bf16) {
     if (full)
-      store_tiles_impl<false, true>(acc, out, t, m0, n0, mlim, nlim, grp, r);
+      store_tiles_impl<false, true>(acc, out, t, m0, n0, mlim, nlim, grp, r, unscale);
     else
-      store_tiles_impl<true, true>(acc, out, t, m0, n0, mlim, nlim, grp, r);
+      store_tiles_impl<true, true>(acc, out, t, m0, n0, mlim, nlim, grp, r, unscale);
   } else {
     if (full)
-      store_tiles_impl<false, false>(acc, out, t, m0, n0, mlim, nlim, grp, r);
+      store_tiles_impl<false, false>(acc, out, t, m0, n0, mlim, nlim, grp, r, unscale);
     else
-      store_tiles_impl<true, false>(acc, out, t, m0, n0, mlim, nlim, grp, r);
+      store_tiles_impl<true, false>(acc, out, t, m0, n0, mlim, nlim, grp, r, unscale);
   }
 }
 
@@ -731,6 +731,13 @@ constexpr int kHugeLoads = kHugeALoads + kHugeWLoads;                 // 9
 // buffer resource word 3 for raw (untyped) dword loads on gfx9-family parts
 constexpr int kBufferFlags = 0x00020000;
 
+// WSIDE (measurement variant, tq4_linear_variant): the rotation undone on the
+// decoded weight tiles instead of applied to the activations.  The
+// activations are then s .* x in fp16 (act_sign_kernel), and each lane's two
+// k-steps of a block half (elements 16 h + 8 t + e) are rotated back by a
+// butterfly over e and t in-lane and over h between lane groups 2 b and
+// 2 b + 1 (lanes l and l ^ 16).
+template <bool WSIDE>
 __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t abuf0[kHugeTM * kHugeRowA];
   __shared__ __attribute__((aligned(16))) uint8_t abuf1[kHugeTM * kHugeRowA];
@@ -844,13 +851,71 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
       cw[j][0] = p[2 * half];
       cw[j][1] = p[2 * half + 1];
       const uint32_t sw = (c < chunks && ((w_okm >> j) & 1u)) ? p[4] : 0u;
-      sc[j] = scale_pair(half ? (sw >> 16) : (sw & 0xFFFFu));
+      if constexpr (WSIDE) {
+        // z_hat * 2^3: the butterfly's sums grow by up to 32
+        const _Float16 h = static_cast<_Float16>(
+            __uint_as_float((half ? (sw >> 16) : (sw & 0xFFFFu)) << 16) * 8.0f);
+        sc[j][0] = h;
+        sc[j][1] = h;
+      } else {
+        sc[j] = scale_pair(half ? (sw >> 16) : (sw & 0xFFFFu));
+      }
     }
+    half8 bws[kHugeNSub];  // WSIDE: the second step's rotated weights
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       half8 bq[kHugeNSub];
 #pragma unroll
-      for (int j = 0; j < kHugeNSub; ++j) bq[j] = dequant8<kHugeLut>(cw[j][t], sc[j], lutp);
+      for (int j = 0; j < kHugeNSub; ++j) {
+        if constexpr (WSIDE) {
+          if (t == 0) {
+            // vp[e] = (element 16 half + e, element 16 half + 8 + e): the
+            // butterfly in packed fp16, stages over e in-lane, the stage over
+            // the pair within each register, the stage over half across lanes
+            half2v vp[8];
+            {
+              const half8 q0 = dequant8<kHugeLut>(cw[j][0], sc[j], lutp);
+              const half8 q1 = dequant8<kHugeLut>(cw[j][1], sc[j], lutp);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                vp[e][0] = q0[e];
+                vp[e][1] = q1[e];
+              }
+            }
+#pragma unroll
+            for (int hb = 1; hb < 8; hb <<= 1)
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if ((e & hb) == 0) {
+                  const half2v lo = vp[e], hi = vp[e + hb];
+                  vp[e] = lo + hi;
+                  vp[e + hb] = lo - hi;
+                }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const _Float16 a0 = vp[e][0], a1 = vp[e][1];
+              vp[e][0] = a0 + a1;
+              vp[e][1] = a0 - a1;
+            }
+            const half2v sg = half ? half2v{-1.f16, -1.f16} : half2v{1.f16, 1.f16};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              uint32_t lo, hi;
+              lane_pair16(__builtin_bit_cast(uint32_t, vp[e]), lo, hi);
+              vp[e] = __builtin_bit_cast(half2v, hi) * sg + __builtin_bit_cast(half2v, lo);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              bq[j][e] = vp[e][0];
+              bws[j][e] = vp[e][1];
+            }
+          } else {
+            bq[j] = bws[j];
+          }
+        } else {
+          bq[j] = dequant8<kHugeLut>(cw[j][t], sc[j], lutp);
+        }
+      }
       const int slot = (2 * grp + t) ^ ((r >> 1) % 8);
 #pragma unroll
       for (int i = 0; i < kHugeMSub; ++i) {
@@ -886,8 +951,9 @@ __global__ __launch_bounds__(64 * kHugeWaves) void gemm_huge_kernel(GemmArgs g) 
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the padding chunks' loads
 
+  // WSIDE: sum * 2^-3 / sqrt(32) (the 2^3 shift of its weight operand)
   store_tiles(acc, g.out, g.tail, m_base + wm * (16 * kHugeMSub), n_base + wn * (16 * kHugeNSub),
-              g.m, g.n, grp, r);
+              g.m, g.n, grp, r, WSIDE ? 0x1.6a09e6p-6f : kWeightUnscale);
 }
 
 // y[i] = sum over splits of partial[s][i], in split order, then the tail.
@@ -924,7 +990,7 @@ hipError_t dispatch(int msub, int nsub, int waves_m, const GemmArgs &g, dim3 gri
   }
   if constexpr (MODE == kDense) {
     if (waves_m == 2 && nsub == 4 && msub == 8 && g.ksplit == 1 && g.k % 64 == 0) {
-      hipLaunchKernelGGL(gemm_huge_kernel, grid, dim3(64 * kHugeWaves), 0, s, g);
+      hipLaunchKernelGGL(gemm_huge_kernel<false>, grid, dim3(64 * kHugeWaves), 0, s, g);
       return hipGetLastError();
     }
     if (waves_m != 1) return hipErrorInvalidValue;
@@ -999,6 +1065,32 @@ hipError_t launch_dense(const DensePlan &p, const uint16_t *xt, int64_t m, int64
   const int64_t mn = m * n;
   hipLaunchKernelGGL(reduce_partials_kernel, dim3(static_cast<unsigned>((mn + 255) / 256)),
                      dim3(256), 0, s, partial, p.ksplit, m, n, tail, y);
+  return hipGetLastError();
+}
+
+bool dense_huge_fits(int64_t m, int64_t k, int64_t n) {
+  const DensePlan p = plan_dense(m, k, n);
+  return p.waves_m == 2 && p.ksplit == 1 && k % 64 == 0;
+}
+
+hipError_t launch_dense_weight_side(const uint16_t *xs, int64_t m, int64_t k,
+                                    const uint8_t *packed, int64_t n, float *y, hipStream_t s) {
+  if (!dense_huge_fits(m, k, n)) return hipErrorInvalidValue;
+  const DensePlan p = plan_dense(m, k, n);
+  GemmArgs g{};
+  g.a = xs;
+  g.w = packed;
+  g.out = y;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.ksplit = 1;
+  g.chunks = static_cast<int32_t>(p.chunks);
+  g.tiles_m = static_cast<int32_t>(p.m_tiles);
+  g.tiles_n = static_cast<int32_t>(p.n_tiles);
+  g.cb = codebook();
+  const dim3 grid(static_cast<unsigned>(p.n_tiles * p.m_tiles), 1, 1);
+  hipLaunchKernelGGL(gemm_huge_kernel<true>, grid, dim3(64 * kHugeWaves), 0, s, g);
   return hipGetLastError();
 }
 

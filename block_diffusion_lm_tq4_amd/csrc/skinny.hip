@@ -313,10 +313,24 @@ constexpr int kSlotBytes = kXSliceBytes + kChunkBytes;      // 6656
 constexpr int kDmaMaxK = 2944;
 constexpr int kDmaMaxChunks = kDmaMaxK / 128;               // 23
 
+// Consumer arithmetic of skinny_dma_kernel.  The default is the library's
+// product; the other two exist to measure the alternatives the format
+// admits (tq4_linear_variant): the rotation undone on the weight tiles
+// instead of applied to the activations, and the products on the VALU
+// instead of MFMA.
+constexpr int kArithDefault = 0;
+constexpr int kArithWeightSide = 1;
+constexpr int kArithValu = 2;
+// element order of decode8_perm's output positions
+constexpr int kPermOrder[8] = {0, 2, 4, 6, 1, 3, 5, 7};
 
+
+template <int ARITH>
 __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t slots[kDmaMaxChunks * kSlotBytes];
   __shared__ uint32_t ready[kDmaMaxChunks];
+  // the VALU-product variant decodes through a table of fp16 level pairs
+  __shared__ uint32_t pairs[ARITH == kArithValu ? 256 : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -389,6 +403,10 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
   // ------------------------------------------------------------ consumers
   if (tid < kDmaMaxChunks) ready[tid] = 0u;
   const PermTable pt = make_perm_table(g.cb);
+  if constexpr (ARITH == kArithValu) {
+    for (int i = tid; i < 256; i += 64 * kDmaConsumers)
+      pairs[i] = pack_f16x2(g.cb.c[i & 15], g.cb.c[i >> 4]);
+  }
   // rotation operand: lane group g of the rotated block must hold elements
   // 8g + (0, 2, 4, 6, 1, 3, 5, 7), the order decode8_perm yields the levels
   // in, so MFMA row q of the first product stands for element
@@ -406,69 +424,235 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
       h_hi[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(kRotEntryBF16 | (n_hi << 15)));
     }
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): flags written
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): flags (and pair table) written
   __builtin_amdgcn_s_barrier();
 
   const int half = grp >> 1;
   floatx4 acc[kRowTiles];
 #pragma unroll
   for (int j = 0; j < kRowTiles; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float vacc[4][16];  // kArithValu: rows 4 (lane % 8) + i, all 16 tokens
+  if constexpr (ARITH == kArithValu) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < 16; ++m) vacc[i][m] = 0.f;
+  }
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-  // Per chunk: the chunk's x parts, code words and scales from LDS, the
-  // rotation of its 4 x blocks (MFMA), then the register decode and the
-  // products.  Nothing in the loop touches global memory.
   for (int c = wave; c < chunks; c += kDmaConsumers) {
     // acquire at workgroup scope: the slot reads below cannot move above the
     // load that saw the flag set
     while (__hip_atomic_load(&ready[c], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
       __builtin_amdgcn_s_sleep(1);
-    const uint8_t *sl = slots + c * kSlotBytes;
-    // 1. this lane's x parts, code words and half-block scales
-    bf16x8 xb[4];
-    uint32_t cw[kRowTiles][4], sc[kRowTiles][4];
+    uint8_t *sl = slots + c * kSlotBytes;
+    if constexpr (ARITH == kArithDefault) {
+      // Per chunk: the chunk's x parts, code words and scales from LDS, the
+      // rotation of its 4 x blocks (MFMA), then the register decode and the
+      // products.  Nothing in the loop touches global memory.
+      bf16x8 xb[4];
+      uint32_t cw[kRowTiles][4], sc[kRowTiles][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      xb[t] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4 *>(sl + 256 * r + 16 * ((4 * t + grp) ^ r)));
+      for (int t = 0; t < 4; ++t)
+        xb[t] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4 *>(sl + 256 * r + 16 * ((4 * t + grp) ^ r)));
 #pragma unroll
-    for (int j = 0; j < kRowTiles; ++j) {
-      const uint8_t *wr = sl + kXSliceBytes + (16 * j + r) * kChunkRowBytes;
+      for (int j = 0; j < kRowTiles; ++j) {
+        const uint8_t *wr = sl + kXSliceBytes + (16 * j + r) * kChunkRowBytes;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        cw[j][t] = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 4 * grp);
-        sc[j][t] = *reinterpret_cast<const uint16_t *>(wr + 20 * t + 16 + 2 * half);
-      }
-    }
-    // 2. rotated activations of the chunk's 4 blocks
-    half8 a[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_lo, xb[t], zero, 0, 0, 0);
-      const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_hi, xb[t], zero, 0, 0, 0);
-      a[t] = __builtin_bit_cast(half8, make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
-                                                  pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])));
-    }
-    // 3. decode, scale and accumulate
-#pragma unroll
-    for (int j = 0; j < kRowTiles; ++j)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const half2v s = scale_pair(sc[j][t]);
-        uint32_t d[4];
-        decode8_perm(cw[j][t], pt, d);
-        half8 bq;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const half2v p = __builtin_bit_cast(half2v, d[b]) * s;
-          bq[2 * b] = p[0];
-          bq[2 * b + 1] = p[1];
+        for (int t = 0; t < 4; ++t) {
+          cw[j][t] = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 4 * grp);
+          sc[j][t] = *reinterpret_cast<const uint16_t *>(wr + 20 * t + 16 + 2 * half);
         }
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bq, acc[j], 0, 0, 0);
       }
+      half8 a[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_lo, xb[t], zero, 0, 0, 0);
+        const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_hi, xb[t], zero, 0, 0, 0);
+        a[t] = __builtin_bit_cast(half8, make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
+                                                    pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])));
+      }
+#pragma unroll
+      for (int j = 0; j < kRowTiles; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const half2v s = scale_pair(sc[j][t]);
+          uint32_t d[4];
+          decode8_perm(cw[j][t], pt, d);
+          half8 bq;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const half2v p = __builtin_bit_cast(half2v, d[b]) * s;
+            bq[2 * b] = p[0];
+            bq[2 * b + 1] = p[1];
+          }
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bq, acc[j], 0, 0, 0);
+        }
+    } else if constexpr (ARITH == kArithWeightSide) {
+      // The rotation on the weight side: every decoded block is rotated back
+      // (w = s .* H z / sqrt(32)) by a butterfly across the wave (bits 0-2 of
+      // the element index in-lane, bits 3 and 4 between lane groups), and
+      // the activations enter the products unrotated, as fp16 with the signs
+      // s applied (s .* x . H z = x . s .* H z).
+      half8 a[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(sl + 256 * r + 16 * ((4 * t + grp) ^ r));
+        const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int pos = 0; pos < 8; ++pos) {
+          const int e = kPermOrder[pos];
+          const uint32_t bits = (e & 1) ? (wv[e >> 1] & 0xFFFF0000u) : (wv[e >> 1] << 16);
+          const float xv = __uint_as_float(bits ^ (((g.sign_bits >> (8 * grp + e)) & 1u) << 31));
+          a[t][pos] = static_cast<_Float16>(xv);
+        }
+      }
+      const float sg3 = (grp & 1) ? -1.f : 1.f;  // lower or upper lane of the bit-3 pairs
+      const float sg4 = (grp & 2) ? -1.f : 1.f;  // ... of the bit-4 pairs
+#pragma unroll
+      for (int j = 0; j < kRowTiles; ++j) {
+        const uint8_t *wr = sl + kXSliceBytes + (16 * j + r) * kChunkRowBytes;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t cw = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 4 * grp);
+          const uint32_t scb = *reinterpret_cast<const uint16_t *>(wr + 20 * t + 16 + 2 * half);
+          // z_hat * 2^3 (a 2^5 smaller shift than the other products: the
+          // butterfly's sums grow by up to 32)
+          const float sf = __uint_as_float(scb << 16) * 8.0f;
+          const half2v s = __builtin_convertvector((float2v){sf, sf}, half2v);
+          uint32_t d[4];
+          decode8_perm(cw, pt, d);
+          float v[8];  // v[e]: element 8 grp + e of the block
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const half2v p = __builtin_bit_cast(half2v, d[b]) * s;
+            v[kPermOrder[2 * b]] = static_cast<float>(p[0]);
+            v[kPermOrder[2 * b + 1]] = static_cast<float>(p[1]);
+          }
+#pragma unroll
+          for (int hb = 1; hb < 8; hb <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if ((e & hb) == 0) {
+                const float lo = v[e], hi = v[e + hb];
+                v[e] = lo + hi;
+                v[e + hb] = lo - hi;
+              }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uint32_t lo, hi;
+            lane_pair16(__builtin_bit_cast(uint32_t, v[e]), lo, hi);
+            v[e] = __builtin_fmaf(__uint_as_float(hi), sg3, __uint_as_float(lo));
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uint32_t lo, hi;
+            lane_pair32(__builtin_bit_cast(uint32_t, v[e]), lo, hi);
+            v[e] = __builtin_fmaf(__uint_as_float(hi), sg4, __uint_as_float(lo));
+          }
+          half8 bq;
+#pragma unroll
+          for (int pos = 0; pos < 8; ++pos) bq[pos] = static_cast<_Float16>(v[kPermOrder[pos]]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bq, acc[j], 0, 0, 0);
+        }
+      }
+    } else {
+      // Products on the VALU.  1. Lane m + 16 t rotates block t of token m
+      // in fp32 (signs, 32-point butterfly, times 2^-3) and writes the fp16
+      // result over the x it read (the same swizzled 16-byte parts).
+      {
+        const int tm = lane % 16, tb = lane / 16;
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 d = *reinterpret_cast<const uint4 *>(sl + 256 * tm + 16 * ((4 * tb + q) ^ tm));
+          const uint32_t wv[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[8 * q + 2 * i] = __uint_as_float(wv[i] << 16);
+            v[8 * q + 2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((g.sign_bits >> i) & 1u) << 31));
+#pragma unroll
+        for (int hb = 1; hb < 32; hb <<= 1)
+#pragma unroll
+          for (int i = 0; i < 32; ++i)
+            if ((i & hb) == 0) {
+              const float lo = v[i], hi = v[i + hb];
+              v[i] = lo + hi;
+              v[i + hb] = lo - hi;
+            }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // this lane's reads are done
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint4 o;
+          o.x = pack_f16x2(v[8 * q] * 0.125f, v[8 * q + 1] * 0.125f);
+          o.y = pack_f16x2(v[8 * q + 2] * 0.125f, v[8 * q + 3] * 0.125f);
+          o.z = pack_f16x2(v[8 * q + 4] * 0.125f, v[8 * q + 5] * 0.125f);
+          o.w = pack_f16x2(v[8 * q + 6] * 0.125f, v[8 * q + 7] * 0.125f);
+          *reinterpret_cast<uint4 *>(sl + 256 * tm + 16 * ((4 * tb + q) ^ tm)) = o;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the rotated activations are in LDS
+      __builtin_amdgcn_wave_barrier();
+      // 2. Lane rg + 8 kq: rows 4 rg .. 4 rg + 3, inputs 16 kq .. 16 kq + 15 of
+      // the chunk (block kq / 2, half kq % 2); level pairs from the table.
+      const int rg = lane % 8, kq = lane / 8;
+      const int blk = kq >> 1, hf = kq & 1;
+      half2v w[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint8_t *wr = sl + kXSliceBytes + (4 * rg + i) * kChunkRowBytes + 20 * blk;
+        const uint2 cwp = *reinterpret_cast<const uint2 *>(wr + 8 * hf);
+        const half2v s = scale_pair(*reinterpret_cast<const uint16_t *>(wr + 16 + 2 * hf));
+        const uint32_t cws[2] = {cwp.x, cwp.y};
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            w[i][4 * q + b] = __builtin_bit_cast(half2v, pairs[(cws[q] >> (8 * b)) & 0xFFu]) * s;
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const uint4 x0 = *reinterpret_cast<const uint4 *>(sl + 256 * m + 16 * ((2 * kq) ^ m));
+        const uint4 x1 = *reinterpret_cast<const uint4 *>(sl + 256 * m + 16 * ((2 * kq + 1) ^ m));
+        const uint32_t xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int p = 0; p < 8; ++p)
+            vacc[i][m] = __builtin_amdgcn_fdot2(w[i][p], __builtin_bit_cast(half2v, xv[p]),
+                                                vacc[i][m], false);
+      }
+    }
   }
 
   __syncthreads();  // every chunk consumed; partial sums reuse the slots
-  float *red = reinterpret_cast<float *>(slots);  // [kDmaConsumers][kRowTiles][4][64]
+  float *red = reinterpret_cast<float *>(slots);
+  if constexpr (ARITH == kArithValu) {
+    // red[wave][kq][rg * 4 + i][m]: 8 waves x 8 x 32 x 16 floats (128 KB)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        red[(((wave * 8 + lane / 8) * 32) + 4 * (lane % 8) + i) * 16 + m] = vacc[i][m];
+    __syncthreads();
+    // thread n * 16 + m adds up row n, token m over the waves and lane groups
+    const int o = tid;  // 512 outputs, 512 consumer threads
+    const int n_l = o / 16, m = o % 16;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDmaConsumers; ++w)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sum += red[(((w * 8 + q) * 32) + n_l) * 16 + m];
+    const int n = n0 + n_l;
+    if (n < g.n && m < g.m) tail_apply(g.tail, g.y, m, n, g.n, sum * kSkinnyUnscale);
+    return;
+  }
+  // [kDmaConsumers][kRowTiles][4][64]
 #pragma unroll
   for (int j = 0; j < kRowTiles; ++j)
 #pragma unroll
@@ -483,7 +667,9 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
     for (int w = 1; w < kDmaConsumers; ++w) sum += red[((w * kRowTiles + j) * 4 + v) * 64 + lane];
     const int n = n0 + r + 16 * j;
     const int m = 4 * grp + v;
-    if (n < g.n && m < g.m) tail_apply(g.tail, g.y, m, n, g.n, sum * kSkinnyUnscale);
+    // weight-side: sum * 2^-3 / sqrt(32) (the 2^3 shift of its weight operand)
+    const float unscale = ARITH == kArithWeightSide ? 0x1.6a09e6p-6f : kSkinnyUnscale;
+    if (n < g.n && m < g.m) tail_apply(g.tail, g.y, m, n, g.n, sum * unscale);
   }
 }
 
@@ -511,6 +697,44 @@ hipError_t launch_ch(const SkinnyArgs &a, int xl, hipStream_t s) {
 
 }  // namespace
 
+bool skinny_fits(int64_t m, int64_t k, int64_t n);
+
+bool skinny_dma_fits(int64_t m, int64_t k, int64_t n, const void *x, const void *packed) {
+  return skinny_fits(m, k, n) && (k / 32) % 4 == 0 && k <= kDmaMaxK &&
+         reinterpret_cast<uintptr_t>(packed) % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;
+}
+
+hipError_t launch_skinny_variant(int arith, const uint16_t *x, int64_t m, int64_t k,
+                                 const uint8_t *packed, int64_t n, uint32_t sign_bits, float *y,
+                                 hipStream_t s) {
+  if (!skinny_dma_fits(m, k, n, x, packed)) return hipErrorInvalidValue;
+  SkinnyArgs a{};
+  a.x = x;
+  a.w = packed;
+  a.y = y;
+  a.m = static_cast<int32_t>(m);
+  a.n = static_cast<int32_t>(n);
+  a.kb = static_cast<int32_t>(k / 32);
+  a.sign_bits = sign_bits;
+  a.cb = codebook();
+  const unsigned grid = static_cast<unsigned>((n + kRowsPerWG - 1) / kRowsPerWG);
+  switch (arith) {
+    case kArithDefault:
+      hipLaunchKernelGGL(skinny_dma_kernel<kArithDefault>, dim3(grid), dim3(kDmaThreads), 0, s, a);
+      break;
+    case kArithWeightSide:
+      hipLaunchKernelGGL(skinny_dma_kernel<kArithWeightSide>, dim3(grid), dim3(kDmaThreads), 0, s,
+                         a);
+      break;
+    case kArithValu:
+      hipLaunchKernelGGL(skinny_dma_kernel<kArithValu>, dim3(grid), dim3(kDmaThreads), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 bool skinny_fits(int64_t m, int64_t k, int64_t n) {
   // 32-bit offsets inside the kernel: the packed matrix stays below 2 GiB
   return m >= 1 && m <= 16 && k >= 32 && k <= kMaxK && n >= 1 &&
@@ -533,7 +757,7 @@ hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t 
   if ((k / 32) % 4 == 0 && k <= kDmaMaxK && reinterpret_cast<uintptr_t>(packed) % 16 == 0 &&
       reinterpret_cast<uintptr_t>(x) % 16 == 0) {
     const unsigned grid = static_cast<unsigned>((n + kRowsPerWG - 1) / kRowsPerWG);
-    hipLaunchKernelGGL(skinny_dma_kernel, dim3(grid), dim3(kDmaThreads), 0, s, a);
+    hipLaunchKernelGGL(skinny_dma_kernel<kArithDefault>, dim3(grid), dim3(kDmaThreads), 0, s, a);
     return hipGetLastError();
   }
   const int64_t chunks = (k / 32 + 3) / 4;                          // <= 32

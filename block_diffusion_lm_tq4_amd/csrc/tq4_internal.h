@@ -83,6 +83,25 @@ __device__ inline void decode8_perm(uint32_t w, const PermTable &t, uint32_t (&d
   d[3] = __builtin_amdgcn_perm(od_hi, od_lo, 0x07030602u);  // elements 5, 7
 }
 
+// The values of lanes l and l ^ 16 (lower, upper) for every lane, by one
+// v_permlane16_swap of two copies of v; with 32 the same for lanes l and
+// l ^ 32.  The copy is opaque to the compiler: given the same register for
+// both operands it has been seen to treat the two results as one value.
+__device__ inline void lane_pair16(uint32_t v, uint32_t &lower, uint32_t &upper) {
+  uint32_t c;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "v"(v));
+  auto p = __builtin_amdgcn_permlane16_swap(v, c, false, false);
+  lower = p[0];
+  upper = p[1];
+}
+__device__ inline void lane_pair32(uint32_t v, uint32_t &lower, uint32_t &upper) {
+  uint32_t c;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "v"(v));
+  auto p = __builtin_amdgcn_permlane32_swap(v, c, false, false);
+  lower = p[0];
+  upper = p[1];
+}
+
 // xt = H32 diag(s) x / sqrt(32) of one 32-element block: bf16 in (16-byte
 // aligned), fp32 butterfly in natural (Sylvester) order, fp16 out.  The format
 // rotates every weight block by this orthogonal matrix (Nemotron-TheHobbit-
@@ -224,6 +243,22 @@ bool skinny_fits(int64_t m, int64_t k, int64_t n);
 hipError_t launch_skinny(const uint16_t *x, int64_t m, int64_t k, const uint8_t *packed,
                          int64_t n, uint32_t sign_bits, float *y, hipStream_t s,
                          const Tail &tail = Tail{});
+
+// Measurement variants of the M <= 16 streaming kernel (tq4_linear_variant):
+// arith 0 the library's product, 1 the rotation undone on the weight tiles,
+// 2 the products on the VALU.  Only for shapes skinny_dma_fits accepts.
+bool skinny_dma_fits(int64_t m, int64_t k, int64_t n, const void *x, const void *packed);
+hipError_t launch_skinny_variant(int arith, const uint16_t *x, int64_t m, int64_t k,
+                                 const uint8_t *packed, int64_t n, uint32_t sign_bits, float *y,
+                                 hipStream_t s);
+
+// Weight-side measurement variant of the large-M product: xs = s .* x in
+// fp16, then the 256 x 256 tile kernel rotating its decoded weights back.
+hipError_t launch_act_sign_f16(const uint16_t *x, int64_t m, int64_t k, uint32_t sign_bits,
+                               uint16_t *xs, hipStream_t s);
+bool dense_huge_fits(int64_t m, int64_t k, int64_t n);
+hipError_t launch_dense_weight_side(const uint16_t *xs, int64_t m, int64_t k,
+                                    const uint8_t *packed, int64_t n, float *y, hipStream_t s);
 
 // MoE pieces.
 struct MoETile {  // one m-tile of one expert's segment in bucket order

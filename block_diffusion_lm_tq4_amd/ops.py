@@ -257,6 +257,32 @@ def linear_fp8_quantized(x_codes: torch.Tensor, x_scales: torch.Tensor, k: int,
     return out
 
 
+VARIANTS = {"default": 0, "weight_rotation": 1, "valu_product": 2}
+
+
+def linear_variant(x: torch.Tensor, packed: torch.Tensor, sign_bits: int, variant: str,
+                   out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The layer with another rotation placement or product arithmetic
+    (tq4_linear_variant): "default", "weight_rotation" or "valu_product"."""
+    _cuda_contig(x, "x", torch.bfloat16)
+    _cuda_contig(packed, "packed", torch.uint8)
+    m, k = x.shape
+    n = packed.shape[0]
+    _require(packed.dim() == 3 and packed.shape[1] * BLOCK == k and packed.shape[2] == BLOCK_BYTES,
+             "packed must be [n, k/32, 20]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _cuda_contig(out, "out", torch.float32)
+    need = max(linear_workspace_size(m, k, n), m * k * 2)
+    if workspace is None:
+        workspace = _WS.get(x.device, "linear", need)
+    check("tq4_linear_variant", lib().tq4_linear_variant(
+        x.data_ptr(), m, k, packed.data_ptr(), n, sign_bits & 0xFFFFFFFF, out.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), VARIANTS[variant], _stream(x.device)))
+    return out
+
+
 def linear_noalloc(x: torch.Tensor, packed: torch.Tensor, sign_bits: int,
                    out: torch.Tensor | None = None) -> torch.Tensor:
     """tq4_linear on the library's static scratch, no workspace (tq4_linear_noalloc)."""

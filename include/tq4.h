@@ -393,6 +393,32 @@ int tq4_moe_block(const uint16_t *x_bf16, int64_t t, int64_t k, const float *log
                   const uint8_t *w2_packed, uint32_t sign_bits, float *out, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/* Measurement aid: the same layer computed with another placement of the
+ * rotation or another arithmetic for the product, so that the library's
+ * choice can be measured against the alternatives the format admits (model
+ * card, What "Config-I" means: the rotation belongs to every weight block;
+ * it may equally be applied to the activations, since it is orthogonal).
+ *   TQ4_VARIANT_DEFAULT          tq4_linear itself
+ *   TQ4_VARIANT_WEIGHT_ROTATION  the rotation undone on the decoded weight
+ *       tiles by a butterfly across the wavefront (w = s .* H z / sqrt(32)),
+ *       the activations entering the products unrotated (as s .* x, fp16);
+ *       m <= 16 with k a multiple of 128 up to 2944 and 16-byte aligned x
+ *       and packed, or the 256 x 256 tile shapes of large m (workspace of
+ *       m * k * 2 bytes, 256-byte aligned)
+ *   TQ4_VARIANT_VALU_PRODUCT     the activation rotation and the products on
+ *       the vector ALU (fp16 pairs, fp32 sums) instead of MFMA; the m <= 16
+ *       shapes above only
+ * Arguments as tq4_linear; results meet the same error bar (the large-m
+ * weight-side butterfly runs in fp16 and adds up to about 5e-4 relative
+ * error).  Errors as tq4_linear, and TQ4_E_SHAPE for an unknown variant or
+ * a shape the variant does not cover. */
+#define TQ4_VARIANT_DEFAULT 0
+#define TQ4_VARIANT_WEIGHT_ROTATION 1
+#define TQ4_VARIANT_VALU_PRODUCT 2
+int tq4_linear_variant(const uint16_t *x_bf16, int64_t m, int64_t k, const uint8_t *packed,
+                       int64_t n, uint32_t sign_bits, float *y, void *workspace,
+                       size_t workspace_bytes, int variant, void *stream);
+
 /* Measurement aid, not a step of the method: reads `bytes` bytes of device
  * memory at `src` once (16 bytes per thread, one launch) and discards them.
  * Timing one call over the footprint of a packed matrix gives the read

@@ -143,6 +143,23 @@ def test_linear_noalloc_argument_errors(L):
     assert L.tq4_linear_workspace_size(4096, 2688, 8192) <= (32 << 20)
 
 
+def test_linear_variant_argument_errors(L):
+    def call(variant, **kw):
+        a = dict(x=FAKE, m=16, k=2688, p=FAKE, n=8192, y=FAKE)
+        a.update(kw)
+        return L.tq4_linear_variant(a["x"], a["m"], a["k"], a["p"], a["n"], 0, a["y"], None, 0,
+                                    variant, None)
+
+    assert call(7) == E_SHAPE                        # no such variant
+    assert call(-1) == E_SHAPE
+    for v in (1, 2):
+        assert call(v, k=2690) == E_SHAPE
+        assert call(v, x=None) == E_NULL
+        assert call(v, y=None) == E_NULL
+        assert call(v, x=MIS) == E_ALIGN
+        assert call(v, m=0) == OK
+
+
 def test_linear_epilogue_argument_errors(L):
     ws = L.tq4_linear_workspace_size(100, 2688, 8192)
     y = FAKE
