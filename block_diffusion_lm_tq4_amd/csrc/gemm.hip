@@ -63,7 +63,7 @@ struct GemmArgs {
   int32_t topk;
   int32_t ksplit;
   int32_t chunks;            // ceil(k / 128)
-  int32_t tiles_m, tiles_n;  // dense: workgroup tiles along m and n
+  int32_t tiles_m, tiles_n;  // workgroup tiles along m and n (MoE: column blocks in tiles_n)
   uint32_t sign_bits;        // MoE up: rotation signs of the hidden rows
   Codebook cb;
 };
@@ -191,6 +191,138 @@ struct WRaw {
   uint32_t v[5];
 };
 
+// The (tile, column block) pair of a grouped-kernel workgroup.  The grid is
+// one-dimensional and a multiple of 8 long; workgroup ids go round robin over
+// the 8 XCDs, and XCD x takes the x-th eighth of the pairs in order (tile
+// major): its workgroups in flight then share each tile's activation rows
+// and, for an expert with several tiles, its weight rows, in their own L2.
+// Returns false for workgroups past the device-side tile count.
+__device__ inline bool moe_item(const GemmArgs &g, int &tile, int64_t &col_block) {
+  const int cols = g.tiles_n;
+  const int total = *g.n_tiles * cols;
+  const int lin = static_cast<int>(blockIdx.x);
+  const int per = (total + 7) / 8;
+  const int j = lin / 8;
+  const int item = (lin % 8) * per + j;
+  if (j >= per || item >= total) return false;
+  tile = item / cols;
+  col_block = item % cols;
+  return true;
+}
+
+// MoE epilogues.  Lane (grp, r) of wave `wave` holds acc[i][j][v] =
+// C[16 i + 4 grp + v][16 NSUB wave + 16 j + r] of the workgroup tile (rows
+// from m_base, columns from n_base); abuf0 and abuf1 are two LDS buffers of
+// at least kWaves * 8 * MSUB * 32 floats that every wave is done with once
+// the up epilogue's leading barrier has passed.
+template <int MSUB, int NSUB, int MODE>
+__device__ inline void moe_store(const floatx4 (&acc)[MSUB][NSUB], const GemmArgs &g,
+                                 int64_t m_base, int64_t rows_valid, int64_t n_base, int wave,
+                                 int lane, uint8_t *abuf0, uint8_t *abuf1) {
+  const int r = lane % 16;
+  const int grp = lane / 16;
+  if constexpr (MODE == kMoEUp) {
+    // h = relu(u)^2, then its rotation ht = H32 diag(s) h / sqrt(32), stored
+    // as fp16: a wave's 32 output columns are one 32-block of h.  The wave
+    // parks its rows of h in LDS (rows 0-7 of every 16-row tile in abuf0,
+    // rows 8-15 in abuf1; 8 * MSUB staged rows x 32 per wave and buffer,
+    // 16-byte column groups XOR-swizzled by (row / 2) % 8); then two lanes
+    // per staged row rotate it in registers: lane parity p holds elements
+    // 16p .. 16p + 15, rotated in-lane over bits 0-3 of the element index,
+    // and bit 4 pairs the two lanes (a quad-permute exchange).  Each lane
+    // writes 32 contiguous bytes.  The stored values carry the factor
+    // 2^-kHiddenShift, which the down product's result undoes.
+    static_assert(NSUB == 2, "one 32-block of hidden units per wave");
+    __syncthreads();  // every wave is done with the activation stages
+    float *const hs0 = reinterpret_cast<float *>(abuf0) + wave * (8 * MSUB * 32);
+    float *const hs1 = reinterpret_cast<float *>(abuf1) + wave * (8 * MSUB * 32);
+    const float rs32 = kHiddenRotScale;  // 1/sqrt(32) and the hidden shift
+    const int p = lane & 1;
+    const int srow = (lane >> 1) < 8 * MSUB ? (lane >> 1) : 0;
+    const int key = 4 * ((srow >> 1) & 7);
+#pragma unroll
+    for (int jp = 0; jp < NSUB / 2; ++jp) {
+      {
+        float *const hw = (grp >> 1) ? hs1 : hs0;
+#pragma unroll
+        for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float u = acc[i][2 * jp + j][v] * kWeightUnscale;
+              const int sr = 8 * i + 4 * (grp & 1) + v;
+              hw[sr * 32 + ((16 * j + r) ^ (4 * ((sr >> 1) & 7)))] = u > 0.f ? u * u : 0.f;
+            }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own writes are visible
+      const int64_t col0 = n_base + wave * (16 * NSUB) + 32 * jp;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float *hs = half ? hs1 : hs0;
+        const int64_t local = 16 * (srow / 8) + 8 * half + srow % 8;
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f =
+              *reinterpret_cast<const float4 *>(hs + srow * 32 + ((16 * p + 4 * q) ^ key));
+          v[4 * q] = f.x;
+          v[4 * q + 1] = f.y;
+          v[4 * q + 2] = f.z;
+          v[4 * q + 3] = f.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if ((g.sign_bits >> (16 * p + e)) & 1u) v[e] = -v[e];
+#pragma unroll
+        for (int hstep = 1; hstep < 16; hstep <<= 1)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if ((e & hstep) == 0) {
+              const float a = v[e], b = v[e + hstep];
+              v[e] = a + b;
+              v[e + hstep] = a - b;
+            }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float o = __builtin_bit_cast(
+              float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[e]), 0xB1, 0xF, 0xF, false));
+          v[e] = p ? o - v[e] : v[e] + o;
+        }
+        if ((lane >> 1) < 8 * MSUB && local < rows_valid && col0 < g.n) {
+          uint4 *dst = reinterpret_cast<uint4 *>(g.out16 + (m_base + local) * g.n + col0 + 16 * p);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            uint32_t w[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t lo =
+                  __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[8 * q + 2 * t] * rs32));
+              const uint32_t hi =
+                  __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[8 * q + 2 * t + 1] * rs32));
+              w[t] = lo | (hi << 16);
+            }
+            dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j) {
+        const int64_t n = n_base + wave * (16 * NSUB) + 16 * j + r;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t local = 16 * i + 4 * grp + v;
+          if (local < rows_valid && n < g.n)
+            g.out[(m_base + local) * g.n + n] = acc[i][j][v] * kHiddenUnscale;
+        }
+      }
+  }
+}
+
 // LUTC copies of the pair table are interleaved (entry e of copy q at
 // e * LUTC + q; lane L uses copy L % LUTC), so that random lookups by the
 // lanes of a wave spread over the LDS banks.  The small-tile configurations
@@ -241,12 +373,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
     rows_valid = g.m - m_base;
     split = blockIdx.z;
   } else {
-    if (static_cast<int32_t>(blockIdx.y) >= *g.n_tiles) return;
-    const MoETile t = g.tiles[blockIdx.y];
+    int ti;
+    int64_t cb;
+    if (!moe_item(g, ti, cb)) return;
+    const MoETile t = g.tiles[ti];
     m_base = t.row0;
     rows_valid = t.rows;
     wmat = g.w + static_cast<int64_t>(t.expert) * g.expert_stride;
-    n_base = static_cast<int64_t>(blockIdx.x) * TN;
+    n_base = cb * TN;
   }
 
   // ---- codebook pair table, LUTC interleaved copies -----------------------
@@ -390,103 +524,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
     float *dst = split_k ? g.partial + static_cast<int64_t>(split) * g.m * g.n : g.out;
     store_tiles(acc, dst, split_k ? Tail{} : g.tail, m_base, n_base + wave * (16 * NSUB), g.m,
                 g.n, grp, r);
-  } else if constexpr (MODE == kMoEUp) {
-    // h = relu(u)^2, then its rotation ht = H32 diag(s) h / sqrt(32), stored
-    // as fp16: a wave's 32 output columns are one 32-block of h (NSUB == 2).
-    // The wave parks its rows of h in LDS (rows 0-7 of every 16-row tile in
-    // abuf0, rows 8-15 in abuf1; 8 * MSUB staged rows x 32 per wave and
-    // buffer, 16-byte column groups XOR-swizzled by (row / 2) % 8); then two
-    // lanes per staged row rotate it in registers: lane parity p holds
-    // elements 16p .. 16p + 15, rotated in-lane over bits 0-3 of the element
-    // index, and bit 4 pairs the two lanes (a quad-permute exchange).  Each
-    // lane writes 32 contiguous bytes.  The stored values carry the factor
-    // 2^-kHiddenShift, which the down product's result undoes.
-    static_assert(NSUB == 2, "one 32-block of hidden units per wave");
-    static_assert(kWaves * 8 * MSUB * 32 * 4 <= TM * kChunkBytes, "staging fits");
-    __syncthreads();  // every wave is done with the activation stages
-    float *const hs0 = reinterpret_cast<float *>(abuf0) + wave * (8 * MSUB * 32);
-    float *const hs1 = reinterpret_cast<float *>(abuf1) + wave * (8 * MSUB * 32);
-    {
-      float *const hw = (grp >> 1) ? hs1 : hs0;
-#pragma unroll
-      for (int i = 0; i < MSUB; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float u = acc[i][j][v] * kWeightUnscale;
-            const int srow = 8 * i + 4 * (grp & 1) + v;
-            hw[srow * 32 + ((16 * j + r) ^ (4 * ((srow >> 1) & 7)))] = u > 0.f ? u * u : 0.f;
-          }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own writes are visible
-    const int64_t col0 = n_base + wave * 32;
-    const float rs32 = kHiddenRotScale;  // 1/sqrt(32) and the hidden shift
-    const int p = lane & 1;
-    const int srow = (lane >> 1) < 8 * MSUB ? (lane >> 1) : 0;
-    const int key = 4 * ((srow >> 1) & 7);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const float *hs = half ? hs1 : hs0;
-      const int64_t local = 16 * (srow / 8) + 8 * half + srow % 8;
-      float v[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f =
-            *reinterpret_cast<const float4 *>(hs + srow * 32 + ((16 * p + 4 * q) ^ key));
-        v[4 * q] = f.x;
-        v[4 * q + 1] = f.y;
-        v[4 * q + 2] = f.z;
-        v[4 * q + 3] = f.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if ((g.sign_bits >> (16 * p + e)) & 1u) v[e] = -v[e];
-#pragma unroll
-      for (int hstep = 1; hstep < 16; hstep <<= 1)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if ((e & hstep) == 0) {
-            const float a = v[e], b = v[e + hstep];
-            v[e] = a + b;
-            v[e + hstep] = a - b;
-          }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float o = __builtin_bit_cast(
-            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[e]), 0xB1, 0xF, 0xF, false));
-        v[e] = p ? o - v[e] : v[e] + o;
-      }
-      if ((lane >> 1) < 8 * MSUB && local < rows_valid && col0 < g.n) {
-        uint4 *dst = reinterpret_cast<uint4 *>(g.out16 + (m_base + local) * g.n + col0 + 16 * p);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          uint32_t w[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t lo =
-                __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[8 * q + 2 * t] * rs32));
-            const uint32_t hi =
-                __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[8 * q + 2 * t + 1] * rs32));
-            w[t] = lo | (hi << 16);
-          }
-          dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
-    }
   } else {
-#pragma unroll
-    for (int i = 0; i < MSUB; ++i)
-#pragma unroll
-      for (int j = 0; j < NSUB; ++j) {
-        const int64_t n = n_base + wave * (16 * NSUB) + 16 * j + r;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t local = 16 * i + 4 * grp + v;
-          if (local < rows_valid && n < g.n)
-            g.out[(m_base + local) * g.n + n] = acc[i][j][v] * kHiddenUnscale;
-        }
-      }
+    static_assert(kWaves * 8 * MSUB * 32 * 4 <= TM * kChunkBytes, "staging fits");
+    moe_store<MSUB, NSUB, MODE>(acc, g, m_base, rows_valid, n_base, wave, lane, abuf0, abuf1);
   }
 }
 
@@ -1128,9 +1168,12 @@ hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_
   g.ksplit = 1;
   g.chunks = static_cast<int32_t>((k / 32 + 3) / 4);
   g.cb = codebook();
+  // one workgroup per (tile, column block) pair that can exist, rounded up
+  // to a multiple of 8 (see moe_item)
   const int64_t wg_n = 16 * p.nsub * p.waves_n;
-  const dim3 grid(static_cast<unsigned>((n + wg_n - 1) / wg_n), static_cast<unsigned>(p.max_tiles),
-                  1);
+  const int64_t cols = (n + wg_n - 1) / wg_n;
+  g.tiles_n = static_cast<int32_t>(cols);
+  const dim3 grid(static_cast<unsigned>((cols * p.max_tiles + 7) / 8 * 8), 1, 1);
   if (mode == 0) return dispatch<kMoEUp>(p.msub, p.nsub, p.waves_m, g, grid, s);
   return dispatch<kMoEDown>(p.msub, p.nsub, p.waves_m, g, grid, s);
 }
