@@ -192,22 +192,20 @@ struct WRaw {
 };
 
 // The (tile, column block) pair of a grouped-kernel workgroup.  The grid is
-// one-dimensional and a multiple of 8 long; workgroup ids go round robin over
-// the 8 XCDs, and XCD x takes the x-th eighth of the pairs in order (tile
-// major): its workgroups in flight then share each tile's activation rows
-// and, for an expert with several tiles, its weight rows, in their own L2.
-// Returns false for workgroups past the device-side tile count.
+// one-dimensional, 8 * ceil(max tiles / 8) * cols long.  Workgroup ids go
+// round robin over the 8 XCDs: XCD x takes tiles x, x + 8, x + 16, ..., each
+// with all of its column blocks in a row (ids 8 j + x, j = 0, 1, ...).  So
+// the workgroups in flight on one L2 share each tile's gathered activation
+// rows, and a popular expert, whose tiles are consecutive, is spread evenly
+// over the XCDs and read about once by each of them.  Returns false for
+// workgroups past the device-side tile count.
 __device__ inline bool moe_item(const GemmArgs &g, int &tile, int64_t &col_block) {
   const int cols = g.tiles_n;
-  const int total = *g.n_tiles * cols;
   const int lin = static_cast<int>(blockIdx.x);
-  const int per = (total + 7) / 8;
   const int j = lin / 8;
-  const int item = (lin % 8) * per + j;
-  if (j >= per || item >= total) return false;
-  tile = item / cols;
-  col_block = item % cols;
-  return true;
+  tile = 8 * (j / cols) + lin % 8;
+  col_block = j % cols;
+  return tile < *g.n_tiles;
 }
 
 // MoE epilogues.  Lane (grp, r) of wave `wave` holds acc[i][j][v] =
@@ -1168,12 +1166,12 @@ hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_
   g.ksplit = 1;
   g.chunks = static_cast<int32_t>((k / 32 + 3) / 4);
   g.cb = codebook();
-  // one workgroup per (tile, column block) pair that can exist, rounded up
-  // to a multiple of 8 (see moe_item)
+  // one workgroup per (tile, column block) pair that can exist, the tile
+  // count rounded up to a multiple of 8 (see moe_item)
   const int64_t wg_n = 16 * p.nsub * p.waves_n;
   const int64_t cols = (n + wg_n - 1) / wg_n;
   g.tiles_n = static_cast<int32_t>(cols);
-  const dim3 grid(static_cast<unsigned>((cols * p.max_tiles + 7) / 8 * 8), 1, 1);
+  const dim3 grid(static_cast<unsigned>((p.max_tiles + 7) / 8 * 8 * cols), 1, 1);
   if (mode == 0) return dispatch<kMoEUp>(p.msub, p.nsub, p.waves_m, g, grid, s);
   return dispatch<kMoEDown>(p.msub, p.nsub, p.waves_m, g, grid, s);
 }
