@@ -80,66 +80,45 @@ __device__ inline void route_one_token(const float *row, int32_t n_experts, int3
   }
 }
 
-// One workgroup.  Pairs are split into kRouteWaves contiguous ranges, one per
-// wave, walked in batches of 64 in pair order:
-//   pass 1  per-wave expert histograms (LDS);
-//   scan    per expert, over the waves in order, then over the experts;
-//   pass 2  each pair's slot = offsets[e] + (pairs of e in earlier waves)
-//           + (pairs of e earlier in this wave), the last term from ballots.
-// This is a stable counting sort: inside an expert, pairs keep their order.
-// With logits != nullptr the workgroup first routes the pairs / topk tokens
-// itself (one wave per token, route_one_token) into ids and gates, which the
-// bucketing then reads back.
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    int32_t *ids, int64_t pairs, int32_t n_experts, int32_t *counts,
-    int32_t *offsets, int32_t *perm, int32_t *inv, MoETile *tiles, int32_t *n_tiles,
-    int32_t tile_rows, int32_t *status, const uint16_t *__restrict__ x, int64_t x_blocks,
-    uint32_t sign_bits, uint16_t *__restrict__ xt, const float *__restrict__ logits,
-    int32_t topk, float *gates) {
-  __shared__ int32_t hist[kRouteWaves][kMaxExperts];
-  __shared__ int32_t base[kMaxExperts + 1];
-  __shared__ int32_t tile_base[kMaxExperts + 1];
+// The bucketing is a stable counting sort of the pairs by expert id.  A range
+// of pairs is split into kRouteWaves contiguous pieces, one per wave, each
+// walked in batches of 64 in pair order:
+//   count    per-wave expert histograms (LDS);
+//   scan     per expert over the waves in order, then over the experts;
+//   scatter  each pair's slot = (start of its expert and piece) + (pairs of
+//            the same expert earlier in its batch, from ballots).
+// Inside an expert, pairs keep their order.  Up to kRouteOneGroupPairs pairs
+// one workgroup does all of it (route_kernel); above, the pairs are cut into
+// chunks of at least kRouteChunkMin pairs and three launches count the chunks
+// (route_count_kernel), scan the counts (route_scan_kernel, one workgroup)
+// and scatter each chunk (route_scatter_kernel).  Between the launches a
+// chunk's per-expert counts, then its per-expert start slots, are kept in
+// the first n_experts entries of the chunk's own range of inv, which only
+// that chunk's scatter overwrites afterwards; so the bucketing needs no
+// memory besides its outputs.
+constexpr int64_t kRouteChunkMin = 4096;
+constexpr int64_t kRouteOneGroupPairs = 2 * kRouteChunkMin - 1;
+static_assert(kRouteChunkMin >= kMaxExperts, "a chunk's range of inv holds its counts");
 
-  const int tid = threadIdx.x;
-  if (blockIdx.x > 0) {
-    // the activation rotation of the same layer rides along in this launch
-    const int64_t blk = static_cast<int64_t>(blockIdx.x - 1) * kRouteThreads + tid;
-    if (blk < x_blocks) rotate_block_bf16(x + blk * 32, sign_bits, xt + blk * 32);
-    return;
-  }
-  const int wave = tid / 64;
-  const int lane = tid % 64;
-  if (logits != nullptr) {
-    for (int64_t tok = wave; tok < pairs / topk; tok += kRouteWaves)
-      route_one_token(logits + tok * n_experts, n_experts, topk, lane, ids + tok * topk,
-                      gates + tok * topk);
-    // the ids are read back only by this workgroup's waves (one compute
-    // unit): a workgroup-scope fence and the barrier make them visible
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __syncthreads();
-  }
-  int key_bits = 0;
-  while ((1 << key_bits) < n_experts) ++key_bits;
-
-  for (int i = tid; i < kRouteWaves * kMaxExperts; i += kRouteThreads)
-    (&hist[0][0])[i] = 0;
-  __syncthreads();
-
-  const int64_t per_wave = (pairs + kRouteWaves - 1) / kRouteWaves;
-  const int64_t p_begin = wave * per_wave;
-  const int64_t p_end = (p_begin + per_wave < pairs) ? p_begin + per_wave : pairs;
-
+// Adds the expert counts of pairs [p_begin, p_end) into hist_w (LDS) and
+// returns the number of this lane's pairs whose id is outside [0, n_experts).
+__device__ inline int32_t count_pairs(const int32_t *ids, int64_t p_begin, int64_t p_end,
+                                      int lane, int32_t n_experts, int32_t *hist_w) {
   int32_t bad = 0;
   for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
     const int64_t p = p0 + lane;
     const int e = (p < p_end) ? ids[p] : -1;
     const bool valid = (p < p_end) && e >= 0 && e < n_experts;
-    if (valid) atomicAdd(&hist[wave][e], 1);
+    if (valid) atomicAdd(&hist_w[e], 1);
     if (p < p_end && !valid) ++bad;
   }
-  __syncthreads();
+  return bad;
+}
 
-  // per expert: exclusive scan over waves, total count
+// Per expert, hist[w][e] becomes the exclusive prefix over the waves w; the
+// total over the waves goes to tot[e] (LDS), when tot is given.
+__device__ inline void scan_over_waves(int32_t (*hist)[kMaxExperts], int32_t n_experts, int tid,
+                                       int32_t *tot) {
   for (int e = tid; e < n_experts; e += kRouteThreads) {
     int32_t run = 0;
     for (int w = 0; w < kRouteWaves; ++w) {
@@ -147,14 +126,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       hist[w][e] = run;
       run += c;
     }
-    counts[e] = run;
-    base[e] = run;
-    tile_base[e] = tile_rows > 0 ? (run + tile_rows - 1) / tile_rows : 0;
+    if (tot != nullptr) tot[e] = run;
+  }
+}
+
+// From the per-expert totals in base[e]: counts, and (by wave 0) exclusive
+// scans of the counts and tile counts over the experts into base, tile_base
+// and offsets, with base[E] = offsets[E] = all valid pairs and
+// tile_base[E] = *n_tiles = all tiles.  Lane l of wave 0 sums experts
+// 8l .. 8l + 7, then the lanes' totals are scanned by shuffles.
+__device__ inline void scan_experts(int32_t n_experts, int32_t tile_rows, int tid, int32_t *base,
+                                    int32_t *tile_base, int32_t *counts, int32_t *offsets,
+                                    int32_t *n_tiles) {
+  for (int e = tid; e < n_experts; e += kRouteThreads) {
+    const int32_t c = base[e];
+    counts[e] = c;
+    tile_base[e] = tile_rows > 0 ? (c + tile_rows - 1) / tile_rows : 0;
   }
   __syncthreads();
-  // exclusive scans of the counts and tile counts over the experts, by wave
-  // 0: lane l sums experts 8l .. 8l + 7, then the lanes' totals are scanned
-  if (wave == 0) {
+  if (tid < 64) {
+    const int lane = tid;
     constexpr int kPer = kMaxExperts / 64;
     int32_t c[kPer], tc[kPer];
     int32_t sum = 0, tsum = 0;
@@ -197,7 +188,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
   }
   __syncthreads();
+}
 
+// Slots of pairs [p_begin, p_end): pair p of expert e goes to base[e] +
+// hist_w[e] + (pairs of e earlier in its batch of 64); hist_w[e] (this
+// wave's start inside the expert, LDS) advances by each batch's count.
+__device__ inline void scatter_pairs(const int32_t *ids, int64_t p_begin, int64_t p_end,
+                                     int lane, int32_t n_experts, int key_bits,
+                                     const int32_t *base, int32_t *hist_w, int32_t *perm,
+                                     int32_t *inv) {
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
     const int64_t p = p0 + lane;
     const int e = (p < p_end) ? ids[p] : -1;
@@ -205,20 +205,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint64_t active = __ballot(valid);
     const int key = valid ? e : 0;
     const uint64_t same = same_key_lanes(key, active, key_bits);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if (valid) {
       const int rank = __popcll(same & below);
-      const int32_t slot = base[e] + hist[wave][e] + rank;
+      const int32_t slot = base[e] + hist_w[e] + rank;
       perm[slot] = static_cast<int32_t>(p);
       inv[p] = slot;
     } else if (p < p_end) {
       inv[p] = -1;
     }
     // the lowest lane of each key group advances the wave's running count
-    if (valid && (same & below) == 0) hist[wave][e] += __popcll(same);
+    if (valid && (same & below) == 0) hist_w[e] += __popcll(same);
   }
+}
 
-  // tile list: expert e owns tiles tile_base[e] .. tile_base[e+1]-1
+// Tile list: expert e owns tiles tile_base[e] .. tile_base[e+1]-1, each of
+// tile_rows bucket rows but the last.
+__device__ inline void write_tiles(int32_t n_experts, int32_t tile_rows, int tid,
+                                   const int32_t *base, const int32_t *tile_base,
+                                   MoETile *tiles) {
   for (int e = tid; tiles != nullptr && tile_rows > 0 && e < n_experts; e += kRouteThreads) {
     const int32_t c = base[e + 1] - base[e];
     for (int32_t i = 0; i * tile_rows < c; ++i) {
@@ -230,7 +234,171 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       tiles[tile_base[e] + i] = t;
     }
   }
+}
+
+__device__ inline int key_bits_for(int32_t n_experts) {
+  int b = 0;
+  while ((1 << b) < n_experts) ++b;
+  return b;
+}
+
+// Piece of wave `wave` when [begin, end) is split into kRouteWaves.
+__device__ inline void wave_piece(int64_t begin, int64_t end, int wave, int64_t &pb,
+                                  int64_t &pe) {
+  const int64_t per = (end - begin + kRouteWaves - 1) / kRouteWaves;
+  pb = begin + wave * per;
+  if (pb > end) pb = end;
+  pe = (pb + per < end) ? pb + per : end;
+}
+
+// Extra workgroups of the first bucketing launch rotate the activation rows
+// of the same layer: one thread per 32-block.
+__device__ inline void rotate_rows(int64_t group, int tid, const uint16_t *__restrict__ x,
+                                   int64_t x_blocks, uint32_t sign_bits,
+                                   uint16_t *__restrict__ xt) {
+  const int64_t blk = group * kRouteThreads + tid;
+  if (blk < x_blocks) rotate_block_bf16(x + blk * 32, sign_bits, xt + blk * 32);
+}
+
+// All of the bucketing in one workgroup (workgroup 0).  With logits !=
+// nullptr it first routes the pairs / topk tokens itself (one wave per token,
+// route_one_token) into ids and gates, which it then reads back.
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    int32_t *ids, int64_t pairs, int32_t n_experts, int32_t *counts, int32_t *offsets,
+    int32_t *perm, int32_t *inv, MoETile *tiles, int32_t *n_tiles, int32_t tile_rows,
+    int32_t *status, const uint16_t *x, int64_t x_blocks, uint32_t sign_bits, uint16_t *xt,
+    const float *__restrict__ logits, int32_t topk, float *gates) {
+  __shared__ int32_t hist[kRouteWaves][kMaxExperts];
+  __shared__ int32_t base[kMaxExperts + 1];
+  __shared__ int32_t tile_base[kMaxExperts + 1];
+
+  const int tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    rotate_rows(blockIdx.x - 1, tid, x, x_blocks, sign_bits, xt);
+    return;
+  }
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  if (logits != nullptr) {
+    for (int64_t tok = wave; tok < pairs / topk; tok += kRouteWaves)
+      route_one_token(logits + tok * n_experts, n_experts, topk, lane, ids + tok * topk,
+                      gates + tok * topk);
+    // the ids are read back only by this workgroup's waves (one compute
+    // unit): a workgroup-scope fence and the barrier make them visible
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __syncthreads();
+  }
+  for (int i = tid; i < kRouteWaves * kMaxExperts; i += kRouteThreads) (&hist[0][0])[i] = 0;
+  __syncthreads();
+
+  int64_t pb, pe;
+  wave_piece(0, pairs, wave, pb, pe);
+  const int32_t bad = count_pairs(ids, pb, pe, lane, n_experts, hist[wave]);
+  __syncthreads();
+  scan_over_waves(hist, n_experts, tid, base);
+  __syncthreads();
+  scan_experts(n_experts, tile_rows, tid, base, tile_base, counts, offsets, n_tiles);
+  scatter_pairs(ids, pb, pe, lane, n_experts, key_bits_for(n_experts), base, hist[wave], perm,
+                inv);
+  write_tiles(n_experts, tile_rows, tid, base, tile_base, tiles);
   if (status != nullptr && bad != 0) atomicAdd(status, bad);
+}
+
+// Chunk g of n_chunks: pairs [g * chunk, (g + 1) * chunk), the last chunk
+// running to the end (so every chunk holds at least `chunk` pairs).
+__device__ inline void chunk_range(int64_t g, int64_t n_chunks, int64_t chunk, int64_t pairs,
+                                   int64_t &begin, int64_t &end) {
+  begin = g * chunk;
+  end = (g + 1 == n_chunks) ? pairs : begin + chunk;
+}
+
+// Launch 1 of 3: each workgroup counts one chunk per expert and leaves the
+// counts in inv[begin + e]; workgroups past the chunks rotate activations.
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(
+    const int32_t *__restrict__ ids, int64_t pairs, int64_t chunk, int64_t n_chunks,
+    int32_t n_experts, int32_t *inv, int32_t *status, const uint16_t *x, int64_t x_blocks,
+    uint32_t sign_bits, uint16_t *xt) {
+  __shared__ int32_t hist[kRouteWaves][kMaxExperts];
+  const int tid = threadIdx.x;
+  if (blockIdx.x >= n_chunks) {
+    rotate_rows(blockIdx.x - n_chunks, tid, x, x_blocks, sign_bits, xt);
+    return;
+  }
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  for (int i = tid; i < kRouteWaves * kMaxExperts; i += kRouteThreads) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  int64_t begin, end, pb, pe;
+  chunk_range(blockIdx.x, n_chunks, chunk, pairs, begin, end);
+  wave_piece(begin, end, wave, pb, pe);
+  const int32_t bad = count_pairs(ids, pb, pe, lane, n_experts, hist[wave]);
+  __syncthreads();
+  for (int e = tid; e < n_experts; e += kRouteThreads) {
+    int32_t c = 0;
+    for (int w = 0; w < kRouteWaves; ++w) c += hist[w][e];
+    inv[begin + e] = c;
+  }
+  if (status != nullptr && bad != 0) atomicAdd(status, bad);
+}
+
+// Launch 2 of 3, one workgroup: wave w sums the counts of chunks
+// [w * per, (w + 1) * per) per expert; the expert totals give counts,
+// offsets and the tile list; then each wave walks its chunks again and
+// replaces every chunk's count of expert e by the chunk's first slot of e.
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(
+    int32_t *inv, int64_t chunk, int64_t n_chunks, int32_t n_experts, int32_t *counts,
+    int32_t *offsets, MoETile *tiles, int32_t *n_tiles, int32_t tile_rows) {
+  __shared__ int32_t hist[kRouteWaves][kMaxExperts];
+  __shared__ int32_t base[kMaxExperts + 1];
+  __shared__ int32_t tile_base[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  int64_t gb, ge;
+  wave_piece(0, n_chunks, wave, gb, ge);
+  for (int e = lane; e < n_experts; e += 64) {
+    int32_t c = 0;
+    for (int64_t g = gb; g < ge; ++g) c += inv[g * chunk + e];
+    hist[wave][e] = c;
+  }
+  __syncthreads();
+  scan_over_waves(hist, n_experts, tid, base);
+  __syncthreads();
+  scan_experts(n_experts, tile_rows, tid, base, tile_base, counts, offsets, n_tiles);
+  for (int e = lane; e < n_experts; e += 64) {
+    int32_t run = base[e] + hist[wave][e];
+    for (int64_t g = gb; g < ge; ++g) {
+      const int32_t c = inv[g * chunk + e];
+      inv[g * chunk + e] = run;
+      run += c;
+    }
+  }
+  write_tiles(n_experts, tile_rows, tid, base, tile_base, tiles);
+}
+
+// Launch 3 of 3: each workgroup takes its chunk's first slots from
+// inv[begin + e], then counts and scatters the chunk like route_kernel.
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
+    const int32_t *__restrict__ ids, int64_t pairs, int64_t chunk, int64_t n_chunks,
+    int32_t n_experts, int32_t *perm, int32_t *inv) {
+  __shared__ int32_t hist[kRouteWaves][kMaxExperts];
+  __shared__ int32_t base[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  int64_t begin, end, pb, pe;
+  chunk_range(blockIdx.x, n_chunks, chunk, pairs, begin, end);
+  for (int e = tid; e < n_experts; e += kRouteThreads) base[e] = inv[begin + e];
+  for (int i = tid; i < kRouteWaves * kMaxExperts; i += kRouteThreads) (&hist[0][0])[i] = 0;
+  // every start slot is read before any pair's slot overwrites inv
+  __syncthreads();
+  wave_piece(begin, end, wave, pb, pe);
+  count_pairs(ids, pb, pe, lane, n_experts, hist[wave]);
+  __syncthreads();
+  scan_over_waves(hist, n_experts, tid, nullptr);
+  __syncthreads();
+  scatter_pairs(ids, pb, pe, lane, n_experts, key_bits_for(n_experts), base, hist[wave], perm,
+                inv);
 }
 
 // out[t, :] = sum_j w[t, j] * o[inv[t*topk + j], :] in slot order; each thread
@@ -278,15 +446,30 @@ hipError_t launch_route(const int32_t *ids, int64_t pairs, int32_t topk, int32_t
                         MoETile *tiles, int32_t *n_tiles, int32_t tile_rows, int32_t *status,
                         hipStream_t s, const uint16_t *x, int64_t x_blocks, uint32_t sign_bits,
                         uint16_t *xt, const float *logits, float *gates) {
-  if (n_experts > kMaxExperts) return hipErrorInvalidValue;
+  if (n_experts < 1 || n_experts > kMaxExperts || pairs < 0) return hipErrorInvalidValue;
   if (logits != nullptr && (gates == nullptr || topk < 1 || pairs % topk != 0))
     return hipErrorInvalidValue;
   const int64_t rot_wgs = x != nullptr ? (x_blocks + kRouteThreads - 1) / kRouteThreads : 0;
-  // the ids are written by the kernel itself when it also routes
-  hipLaunchKernelGGL(route_kernel, dim3(static_cast<unsigned>(1 + rot_wgs)), dim3(kRouteThreads),
-                     0, s, const_cast<int32_t *>(ids), pairs, n_experts, counts, offsets, perm,
-                     inv, tiles, n_tiles, tile_rows, status, x, x_blocks, sign_bits, xt, logits,
-                     topk, gates);
+  if (logits != nullptr || pairs <= kRouteOneGroupPairs) {
+    // the ids are written by the kernel itself when it also routes
+    hipLaunchKernelGGL(route_kernel, dim3(static_cast<unsigned>(1 + rot_wgs)),
+                       dim3(kRouteThreads), 0, s, const_cast<int32_t *>(ids), pairs, n_experts,
+                       counts, offsets, perm, inv, tiles, n_tiles, tile_rows, status, x,
+                       x_blocks, sign_bits, xt, logits, topk, gates);
+    return hipGetLastError();
+  }
+  // chunks of at least kRouteChunkMin pairs, at most 1024 of them
+  int64_t chunk = kRouteChunkMin;
+  while (pairs / chunk > 1024) chunk *= 2;
+  const int64_t n_chunks = pairs / chunk;
+  hipLaunchKernelGGL(route_count_kernel, dim3(static_cast<unsigned>(n_chunks + rot_wgs)),
+                     dim3(kRouteThreads), 0, s, ids, pairs, chunk, n_chunks, n_experts, inv,
+                     status, x, x_blocks, sign_bits, xt);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), 0, s, inv, chunk, n_chunks,
+                     n_experts, counts, offsets, tiles, n_tiles, tile_rows);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(static_cast<unsigned>(n_chunks)),
+                     dim3(kRouteThreads), 0, s, ids, pairs, chunk, n_chunks, n_experts, perm,
+                     inv);
   return hipGetLastError();
 }
 

@@ -267,7 +267,8 @@ struct MoETile {  // one m-tile of one expert's segment in bucket order
   int32_t rows;   // rows in this tile (<= tile height)
   int32_t pad;
 };
-// Bucketing (one workgroup).  With x != nullptr the same launch also rotates
+// Bucketing (one workgroup up to 8191 pairs, else three launches whose first
+// counts chunks of pairs).  With x != nullptr the first launch also rotates
 // the [t, k] bf16 activation rows into xt (extra workgroups, one thread per
 // 32-block).  With logits != nullptr the bucketing workgroup first routes the
 // pairs / topk tokens itself (the router's arithmetic, bit for bit), writing

@@ -324,7 +324,10 @@ int tq4_moe_grouped_fp8(const uint16_t *x_bf16, int64_t t, int64_t k,
  *              are left untouched
  *   inv      : [t * topk] int32, device  -- inv[perm[i]] = i; -1 for pairs
  *              whose id is outside [0, n_experts)
- * One kernel, no host synchronization.  Errors: TQ4_E_NULL, TQ4_E_SHAPE
+ * No host synchronization and no memory besides the outputs: one kernel up
+ * to 8191 pairs; above, three (per-chunk counts, kept in inv until the last
+ * launch overwrites them; one scan; per-chunk scatter).  Results are the
+ * same either way.  Errors: TQ4_E_NULL, TQ4_E_SHAPE
  * (t < 0, topk < 1, n_experts < 1 or > 512), TQ4_E_DEVICE. */
 int tq4_moe_route(const int32_t *topk_ids, int64_t t, int32_t topk, int32_t n_experts,
                   int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,

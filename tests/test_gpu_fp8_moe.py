@@ -113,6 +113,7 @@ def _run(dev, ex, x, ids, g):
     (300, 4, 2, 160, 288),    # 64-row tiles, three per expert
     (1, 3, 1, 32, 32),        # one pair, one 32-block each way
     (70, 5, 3, 128, 640),     # 64-row tiles, a full and a partial one per expert
+    (2100, 8, 4, 64, 96),     # 8400 pairs: the bucketing in chunks
 ])
 def test_moe_fp8_small_matches_oracle(dev, t, n_exp, topk, n1, k):
     ex = _small_experts(dev, n_exp, n1, k, seed=t + n_exp)

@@ -448,6 +448,64 @@ def test_route_invalid_ids_and_small_expert_counts(dev):
         assert np.array_equal(inv.cpu().numpy(), iv)
 
 
+def _route_ids(t, e, topk, routing, seed):
+    rng = np.random.default_rng(seed)
+    if routing == "zipf":
+        pr = 1.0 / np.arange(1, e + 1) ** 1.1
+        ids = rng.choice(e, size=(t, topk), p=pr / pr.sum())
+    elif routing == "invalid":
+        ids = rng.integers(-3, e + 3, size=(t, topk))
+    else:
+        ids = rng.integers(0, e, size=(t, topk))
+    return ids.astype(np.int32)
+
+
+@pytest.mark.parametrize("t,e,topk,routing", [
+    (1365, 128, 6, "uniform"),      # 8190 pairs: one bucketing workgroup
+    (8191, 1, 1, "uniform"),        # its limit, every pair on one expert
+    (8192, 1, 1, "uniform"),        # two chunks of 4096, every pair on one expert
+    (8193, 7, 1, "invalid"),        # two chunks, the last one pair longer; bad ids
+    (4096, 128, 6, "zipf"),         # six chunks, skewed experts
+    (3001, 100, 7, "uniform"),      # experts not a multiple of 64, ragged last chunk
+    (20000, 512, 8, "invalid"),     # largest expert count
+    (65536, 128, 6, "uniform"),     # 96 chunks (prefill-sized layer)
+    (700001, 64, 6, "zipf"),        # 4.2 M pairs: chunks of 8192, at most 1024 of them
+])
+def test_route_chunked_bit_exact(dev, t, e, topk, routing):
+    """The bucketing equals the oracle's stable sort on both sides of the
+    one-workgroup limit and for many chunks; perm past offsets[E] keeps the
+    caller's contents."""
+    ids = _route_ids(t, e, topk, routing, seed=t + e)
+    counts, offsets, perm, inv = _ops().moe_route(torch.from_numpy(ids).to(dev), e)
+    c, o, p, iv = O.bucket_pairs(ids, e)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    pm = perm.cpu().numpy()
+    assert np.array_equal(pm[: p.size], p)
+    assert (pm[p.size:] == -7).all()
+    assert np.array_equal(inv.cpu().numpy(), iv)
+
+
+def test_moe_layer_chunked_bucketing(dev):
+    """A layer whose bucketing takes the three-launch form (2600 tokens x
+    top-6 = 15600 pairs): tile list, rotation and products against the
+    oracle on every token."""
+    t, e, k, n1, topk = 2600, 12, 64, 32, 6
+    rng = np.random.default_rng(29)
+    w1 = (0.05 * rng.standard_normal((e, n1, k))).astype(np.float32)
+    w2 = (0.05 * rng.standard_normal((e, k, n1))).astype(np.float32)
+    p1 = np.stack([O.pack(w1[i], SB) for i in range(e)])
+    p2 = np.stack([O.pack(w2[i], SB) for i in range(e)])
+    x = I.activations_bf16(t, k, seed=30)
+    ids = _route_ids(t, e, topk, "zipf", seed=31)
+    ids[5, 2] = -1                          # dropped slot
+    g = rng.random((t, topk)).astype(np.float32)
+    out = _ops().moe_grouped(_bf16(x, dev), torch.from_numpy(ids).to(dev),
+                             torch.from_numpy(g).to(dev), torch.from_numpy(p1).to(dev),
+                             torch.from_numpy(p2).to(dev), SB).cpu().numpy()
+    _check_close(out, O.moe(x, ids, g, list(p1), list(p2), SB), "moe, chunked bucketing")
+
+
 def test_moe_t16_full(dev, experts):
     wl = I.WORKLOADS["moe_t16"]
     ids, g = I.moe_routing(wl)
