@@ -292,9 +292,9 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
 // its weights (32 rows x 80 bytes).
 //
 //  * kDmaProducers waves keep the loads going: producer p takes chunks p,
-//    p + kDmaProducers, ..., keeps three of them in flight, and as each lands
-//    (its loads retire in issue order) raises that chunk's LDS flag and
-//    issues the chunk three ahead.
+//    p + kDmaProducers, ..., keeps kDmaDepth of them in flight, and as each
+//    lands (its loads retire in issue order) raises that chunk's LDS flag and
+//    issues the chunk kDmaDepth ahead.
 //  * kDmaConsumers waves take chunks round robin; each waits for the chunk's
 //    flag, rotates the x blocks (two bf16 MFMAs per block against the +-1
 //    matrix, as in skinny_kernel), decodes its lane's code words in
@@ -303,8 +303,16 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
 //    Consumers issue no vector-memory loads, so nothing they do waits on the
 //    stream.  Measured against the same kernel decoding through an LDS table
 //    of level pairs: equal results bit for bit, 0.1-0.4 us faster per call.
-constexpr int kDmaProducers = 4;
+// Producers and the chunks each keeps in flight.  Measured per call at
+// K=2688 (graph replay, medians of five runs): 4 producers with 1, 2, 3, 4
+// or 5 chunks each 7.52, 7.17, 7.32-7.40, 7.84, 8.24 us; 8 producers with 1
+// or 2 chunks each 6.98-7.06 and 7.53 us.  About 8 chunks in flight per
+// compute unit is best: more requests in flight only queue longer in front
+// of the ones a consumer waits for, fewer leave the stream short.
+constexpr int kDmaProducers = 8;
 constexpr int kDmaConsumers = 8;
+constexpr int kDmaDepth = 1;
+static_assert(kDmaDepth >= 1 && kDmaDepth <= 3, "the producers' waits cover up to 3 chunks");
 constexpr int kDmaThreads = 64 * (kDmaProducers + kDmaConsumers);
 constexpr int kXSliceBytes = 16 * 256;                      // 16 rows x 128 k, bf16
 constexpr int kChunkRowBytes = 80;                          // 4 blocks of one row
@@ -312,6 +320,7 @@ constexpr int kChunkBytes = kRowsPerWG * kChunkRowBytes;    // 2560
 constexpr int kSlotBytes = kXSliceBytes + kChunkBytes;      // 6656
 constexpr int kDmaMaxK = 2944;
 constexpr int kDmaMaxChunks = kDmaMaxK / 128;               // 23
+constexpr int kSimds = 4;  // SIMDs per compute unit
 
 // Consumer arithmetic of skinny_dma_kernel.  The default is the library's
 // product; the other two exist to measure the alternatives the format
@@ -374,26 +383,26 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
     const uint32_t flag_addr = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint32_t *)ready));
     // the first chunk goes out before the barrier that publishes the cleared
-    // flags and the pair table; then three of this producer's chunks stay in
-    // flight: as each lands it is flagged and the chunk three ahead is issued
+    // flags and the pair table; then kDmaDepth of this producer's chunks stay
+    // in flight: as each lands it is flagged and the chunk kDmaDepth ahead is
+    // issued
     if (p < chunks) issue(p);
     __builtin_amdgcn_s_barrier();
-    for (int i = 1; i < 3; ++i)
+    for (int i = 1; i < kDmaDepth; ++i)
       if (p + i * kDmaProducers < chunks) issue(p + i * kDmaProducers);
     for (int c = p; c < chunks; c += kDmaProducers) {
       // loads of chunk c are in once only the later chunks' (7 loads each)
       // are outstanding
-      const int later = (c + kDmaProducers < chunks) + (c + 2 * kDmaProducers < chunks);
-      if (later == 2)
+      if (kDmaDepth > 2 && c + 2 * kDmaProducers < chunks)
         __builtin_amdgcn_s_waitcnt(0x0F7E);  // vmcnt(14)
-      else if (later == 1)
+      else if (kDmaDepth > 1 && c + kDmaProducers < chunks)
         __builtin_amdgcn_s_waitcnt(0x0F77);  // vmcnt(7)
       else
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       // (written in asm: the compiler cannot tell this flag from the slots
       // still being filled and would wait for every load in flight first)
       asm volatile("ds_write_b32 %0, %1" ::"v"(flag_addr + 4 * c), "v"(1u) : "memory");
-      if (c + 3 * kDmaProducers < chunks) issue(c + 3 * kDmaProducers);
+      if (c + kDmaDepth * kDmaProducers < chunks) issue(c + kDmaDepth * kDmaProducers);
     }
     __syncthreads();  // all chunks consumed
     __syncthreads();  // partial sums in LDS
@@ -439,56 +448,85 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
       for (int m = 0; m < 16; ++m) vacc[i][m] = 0.f;
   }
   const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int c = wave; c < chunks; c += kDmaConsumers) {
-    // acquire at workgroup scope: the slot reads below cannot move above the
-    // load that saw the flag set
+  // acquire at workgroup scope: the slot reads after it cannot move above the
+  // load that saw the flag set
+  auto wait_chunk = [&](int c) {
     while (__hip_atomic_load(&ready[c], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
       __builtin_amdgcn_s_sleep(1);
+  };
+  // Default arithmetic on blocks t0 .. t0 + NT - 1 of chunk c: the blocks'
+  // x parts, code words and scales from LDS, the rotation of the x blocks
+  // (MFMA), then the register decode and the products.  Nothing here touches
+  // global memory.
+  auto default_blocks = [&](auto nt, int c, int t0) {
+    constexpr int NT = decltype(nt)::value;
+    wait_chunk(c);
+    const uint8_t *sl = slots + c * kSlotBytes;
+    bf16x8 xb[NT];
+    uint32_t cw[kRowTiles][NT], sc[kRowTiles][NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      xb[t] = __builtin_bit_cast(
+          bf16x8,
+          *reinterpret_cast<const uint4 *>(sl + 256 * r + 16 * ((4 * (t0 + t) + grp) ^ r)));
+#pragma unroll
+    for (int j = 0; j < kRowTiles; ++j) {
+      const uint8_t *wr = sl + kXSliceBytes + (16 * j + r) * kChunkRowBytes + 20 * t0;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        cw[j][t] = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 4 * grp);
+        sc[j][t] = *reinterpret_cast<const uint16_t *>(wr + 20 * t + 16 + 2 * half);
+      }
+    }
+    half8 a[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_lo, xb[t], zero, 0, 0, 0);
+      const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_hi, xb[t], zero, 0, 0, 0);
+      a[t] = __builtin_bit_cast(half8, make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
+                                                  pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])));
+    }
+#pragma unroll
+    for (int j = 0; j < kRowTiles; ++j)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const half2v sp = scale_pair(sc[j][t]);
+        uint32_t d[4];
+        decode8_perm(cw[j][t], pt, d);
+        half8 bq;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const half2v q = __builtin_bit_cast(half2v, d[b]) * sp;
+          bq[2 * b] = q[0];
+          bq[2 * b + 1] = q[1];
+        }
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bq, acc[j], 0, 0, 0);
+      }
+  };
+  if constexpr (ARITH == kArithDefault) {
+    // A workgroup's waves go round robin over the SIMDs (measured), so
+    // consumers w and w + kSimds share one, and whole chunks dealt round
+    // robin give every SIMD the same share.  What the consumers still have to
+    // do once the last chunk is in is the kernel's tail, so the last chunks
+    // are cut finer: each chunk of the last full round of kSimds chunks is
+    // split in halves between the two consumers of one SIMD, and the chunks
+    // of a last, partial round (chunks % kSimds of them) by block over
+    // consumers kSimds .. 2 kSimds - 1, one on each SIMD.
+    const int full = chunks - chunks % kSimds;
+    const int last = full >= kSimds ? full - kSimds : 0;
+    for (int c = wave; c < last; c += kDmaConsumers)
+      default_blocks(std::integral_constant<int, 4>{}, c, 0);
+    if (full >= kSimds)
+      default_blocks(std::integral_constant<int, 2>{}, last + wave % kSimds,
+                     wave < kSimds ? 0 : 2);
+    if (wave >= kSimds)
+      for (int c = full; c < chunks; ++c)
+        default_blocks(std::integral_constant<int, 1>{}, c, wave - kSimds);
+  }
+  for (int c = wave; ARITH != kArithDefault && c < chunks; c += kDmaConsumers) {
+    wait_chunk(c);
     uint8_t *sl = slots + c * kSlotBytes;
-    if constexpr (ARITH == kArithDefault) {
-      // Per chunk: the chunk's x parts, code words and scales from LDS, the
-      // rotation of its 4 x blocks (MFMA), then the register decode and the
-      // products.  Nothing in the loop touches global memory.
-      bf16x8 xb[4];
-      uint32_t cw[kRowTiles][4], sc[kRowTiles][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        xb[t] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4 *>(sl + 256 * r + 16 * ((4 * t + grp) ^ r)));
-#pragma unroll
-      for (int j = 0; j < kRowTiles; ++j) {
-        const uint8_t *wr = sl + kXSliceBytes + (16 * j + r) * kChunkRowBytes;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          cw[j][t] = *reinterpret_cast<const uint32_t *>(wr + 20 * t + 4 * grp);
-          sc[j][t] = *reinterpret_cast<const uint16_t *>(wr + 20 * t + 16 + 2 * half);
-        }
-      }
-      half8 a[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_lo, xb[t], zero, 0, 0, 0);
-        const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h_hi, xb[t], zero, 0, 0, 0);
-        a[t] = __builtin_bit_cast(half8, make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
-                                                    pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])));
-      }
-#pragma unroll
-      for (int j = 0; j < kRowTiles; ++j)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const half2v s = scale_pair(sc[j][t]);
-          uint32_t d[4];
-          decode8_perm(cw[j][t], pt, d);
-          half8 bq;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const half2v p = __builtin_bit_cast(half2v, d[b]) * s;
-            bq[2 * b] = p[0];
-            bq[2 * b + 1] = p[1];
-          }
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bq, acc[j], 0, 0, 0);
-        }
-    } else if constexpr (ARITH == kArithWeightSide) {
+    if constexpr (ARITH == kArithWeightSide) {
       // The rotation on the weight side: every decoded block is rotated back
       // (w = s .* H z / sqrt(32)) by a butterfly across the wave (bits 0-2 of
       // the element index in-lane, bits 3 and 4 between lane groups), and
@@ -556,7 +594,7 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bq, acc[j], 0, 0, 0);
         }
       }
-    } else {
+    } else if constexpr (ARITH == kArithValu) {
       // Products on the VALU.  1. Lane m + 16 t rotates block t of token m
       // in fp32 (signs, 32-point butterfly, times 2^-3) and writes the fp16
       // result over the x it read (the same swizzled 16-byte parts).
