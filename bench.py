@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+GRAPH_LEAD_CYCLES = 2_000_000  # GPU spin before a timed replay (~1 ms of shader clock)
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
 MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, TFLOP/s
 
@@ -90,11 +91,16 @@ def time_loop(torch, fn, steps: int, warmup: int) -> float:
     The calls are captured once into a HIP graph (the library launches on
     torch's current stream, which is the capture stream) and the graph is
     replayed, so the GPU runs them back to back without host launch overhead.
-    `warmup` eager calls and one untimed replay come first; then a 512 MiB
-    write evicts the Infinity Cache, so the timed replay reads every input
-    that the graph's calls do not share from HBM, whatever the step count.
-    HIP events on the replay stream bracket the timed replay, with device
-    synchronization on both sides.
+    `warmup` eager calls and one untimed replay come first, then a device
+    synchronization.  A 512 MiB read then evicts the Infinity Cache, so the
+    timed replay reads every input that the graph's calls do not share from
+    HBM, whatever the step count.  HIP events on the replay stream bracket
+    the timed replay.  The start event and the replay are queued behind the
+    flush and a 1 ms spin on the GPU, which leave the host time to submit
+    the whole graph; so the timed region holds the calls alone, not the
+    host's graph-launch work (measured without them: about 26 us per replay
+    at 20 calls, 1.3 us per call, partly as gaps between the calls).  A
+    device synchronization ends it.
     """
     for i in range(warmup):
         fn(i)
@@ -104,10 +110,11 @@ def time_loop(torch, fn, steps: int, warmup: int) -> float:
         for i in range(steps):
             fn(i)
     graph.replay()
-    mall_flush(torch)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    mall_flush(torch)
+    torch.cuda._sleep(GRAPH_LEAD_CYCLES)
     start.record()
     graph.replay()
     stop.record()
