@@ -511,7 +511,9 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
     // are cut finer: each chunk of the last full round of kSimds chunks is
     // split in halves between the two consumers of one SIMD, and the chunks
     // of a last, partial round (chunks % kSimds of them) by block over
-    // consumers kSimds .. 2 kSimds - 1, one on each SIMD.
+    // consumers 0 .. kSimds - 1, one on each SIMD: their whole chunks land
+    // first, so they are the ones done first (measured: the kernel's
+    // consumers w >= kSimds finish about 1 us after the others otherwise).
     const int full = chunks - chunks % kSimds;
     const int last = full >= kSimds ? full - kSimds : 0;
     for (int c = wave; c < last; c += kDmaConsumers)
@@ -519,9 +521,9 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
     if (full >= kSimds)
       default_blocks(std::integral_constant<int, 2>{}, last + wave % kSimds,
                      wave < kSimds ? 0 : 2);
-    if (wave >= kSimds)
+    if (wave < kSimds)
       for (int c = full; c < chunks; ++c)
-        default_blocks(std::integral_constant<int, 1>{}, c, wave - kSimds);
+        default_blocks(std::integral_constant<int, 1>{}, c, wave);
   }
   for (int c = wave; ARITH != kArithDefault && c < chunks; c += kDmaConsumers) {
     wait_chunk(c);
