@@ -164,6 +164,10 @@ def test_linear_dense_m16_full(dev):
     (200, 1856, 300), (3, 4096, 64), (16, 8192, 64), (9, 2688, 8200), (16, 4096, 1000),
     # M <= 16 streaming kernel at its limits, and just past them
     (16, 2944, 100), (7, 3072, 64), (16, 128, 40), (2, 384, 33),
+    # its split of the last chunks over the SIMDs: 4, 6, 8 and 15 chunks of
+    # 128 k (halves only; halves and two split chunks; whole chunks and
+    # halves; all three)
+    (16, 512, 96), (5, 768, 70), (16, 1024, 64), (3, 1920, 50),
     # large-M kernel: chunk counts padded to a multiple of three, ragged M, N, K
     (300, 512, 520), (129, 96, 33), (256, 2688, 512),
     # 256 x 256 tiles (256 or more of them): K = 64 * (5, 2, 3) chunks (padding
