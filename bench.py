@@ -47,11 +47,36 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and with runs of whitespace made one
+    space, so that editing a comment leaves the hash of a kernel alone."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif text[i] in "\"'":
+            q, j = text[i], i + 1
+            while j < n and text[j] != q:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha(sources) -> str:
+    """Hash of the code (comments and layout aside) of a kernel's sources."""
     h = hashlib.sha256()
     for f in sources:
-        with open(os.path.join(ROOT, "block_diffusion_lm_tq4_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "block_diffusion_lm_tq4_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

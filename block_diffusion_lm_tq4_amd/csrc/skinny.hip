@@ -282,24 +282,26 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs g) {
 
 // ---------------------------------------------------------------------------
 // LDS-direct variant, for K a multiple of 128 up to kDmaMaxK.  Measured on
-// this shape, what bounds the kernel is how fast a compute unit takes in its
-// bytes: the weights of its 32 rows plus all of x, which every workgroup
-// needs.  LDS-direct loads of 16 bytes per lane, each instruction covering
-// 1 KB of consecutive memory, take those in markedly faster than loads into
-// registers, so this variant stages everything in LDS, chunk by chunk: a
-// chunk slot holds the chunk's slice of x (16 rows x 256 bytes, its 16-byte
-// parts XOR-swizzled by row so that fragment reads hit distinct banks) and
-// its weights (32 rows x 80 bytes).
+// this shape, the call is the time a compute unit takes to bring in its
+// bytes (the weights of its 32 rows plus all of x, which every workgroup
+// needs) and then to decode the chunks that land last.  LDS-direct loads of
+// 16 bytes per lane, each instruction covering 1 KB of consecutive memory,
+// take those in markedly faster than loads into registers, so this variant
+// stages everything in LDS, chunk by chunk: a chunk slot holds the chunk's
+// slice of x (16 rows x 256 bytes, its 16-byte parts XOR-swizzled by row so
+// that fragment reads hit distinct banks) and its weights (32 rows x 80
+// bytes).
 //
 //  * kDmaProducers waves keep the loads going: producer p takes chunks p,
 //    p + kDmaProducers, ..., keeps kDmaDepth of them in flight, and as each
 //    lands (its loads retire in issue order) raises that chunk's LDS flag and
 //    issues the chunk kDmaDepth ahead.
-//  * kDmaConsumers waves take chunks round robin; each waits for the chunk's
-//    flag, rotates the x blocks (two bf16 MFMAs per block against the +-1
-//    matrix, as in skinny_kernel), decodes its lane's code words in
-//    registers (decode8_perm: byte tables and v_perm_b32, so the LDS serves
-//    only the stream and the chunk reads) and accumulates with f16 MFMAs.
+//  * kDmaConsumers waves take chunks round robin (the last ones cut finer,
+//    see the consumer loop); each waits for the chunk's flag, rotates the x
+//    blocks (two bf16 MFMAs per block against the +-1 matrix, as in
+//    skinny_kernel), decodes its lane's code words in registers
+//    (decode8_perm: byte tables and v_perm_b32, so the LDS serves only the
+//    stream and the chunk reads) and accumulates with f16 MFMAs.
 //    Consumers issue no vector-memory loads, so nothing they do waits on the
 //    stream.  Measured against the same kernel decoding through an LDS table
 //    of level pairs: equal results bit for bit, 0.1-0.4 us faster per call.
