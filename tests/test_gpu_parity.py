@@ -607,6 +607,7 @@ def test_moe_block_matches_oracle_and_the_two_calls(dev, experts, name):
     (65, 128, 6),    # past it: the separate router launch
     (40, 100, 4),    # experts not a multiple of 64
     (64, 100, 8),
+    (1400, 16, 6),   # 8400 pairs: the bucketing in chunks
 ])
 def test_moe_block_router_placements(dev, t, e, topk):
     """tq4_moe_block equals tq4_moe_router + tq4_moe_grouped bit for bit on
