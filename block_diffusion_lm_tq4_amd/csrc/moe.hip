@@ -25,12 +25,70 @@ __device__ inline uint64_t same_key_lanes(int key, uint64_t active, int key_bits
   return m;
 }
 
+// Wave-wide reductions without LDS round trips: within each row of 16 lanes
+// DPP moves pair lane l with l ^ 1, l ^ 2 (quad permutes), 7 - l (mirror
+// within 8) and 15 - l (mirror within 16); then v_permlane16_swap and
+// v_permlane32_swap pair the rows.  Each step combines a lane's value with
+// its partner's by a commutative rule, so every lane ends with the same
+// result, bit for bit.
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <class Combine>
+__device__ inline float wave_reduce(float v, Combine f) {
+  v = f(v, dpp_f<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = f(v, dpp_f<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = f(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = f(v, dpp_f<0x140>(v));  // row_mirror
+  uint32_t lo, hi;
+  lane_pair16(__builtin_bit_cast(uint32_t, v), lo, hi);
+  v = f(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+  lane_pair32(__builtin_bit_cast(uint32_t, v), lo, hi);
+  return f(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+
+// The larger (value, index) pair, ties to the lower index.
+__device__ inline void better_pair(float &bv, int &bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+template <int CTRL>
+__device__ inline void argmax_step(float &bv, int &bi) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oi = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xF, 0xF, false);
+  better_pair(bv, bi, ov, oi);
+}
+
+__device__ inline void wave_argmax(float &bv, int &bi) {
+  argmax_step<0xB1>(bv, bi);
+  argmax_step<0x4E>(bv, bi);
+  argmax_step<0x141>(bv, bi);
+  argmax_step<0x140>(bv, bi);
+  uint32_t vlo, vhi, ilo, ihi;
+  lane_pair16(__builtin_bit_cast(uint32_t, bv), vlo, vhi);
+  lane_pair16(static_cast<uint32_t>(bi), ilo, ihi);
+  bv = __builtin_bit_cast(float, vlo);
+  bi = static_cast<int>(ilo);
+  better_pair(bv, bi, __builtin_bit_cast(float, vhi), static_cast<int>(ihi));
+  lane_pair32(__builtin_bit_cast(uint32_t, bv), vlo, vhi);
+  lane_pair32(static_cast<uint32_t>(bi), ilo, ihi);
+  bv = __builtin_bit_cast(float, vlo);
+  bi = static_cast<int>(ilo);
+  better_pair(bv, bi, __builtin_bit_cast(float, vhi), static_cast<int>(ihi));
+}
+
 // The router in front of the layer (model card, The model underneath: 128
 // experts, top-6) for one token, by one wave: softmax over all expert logits,
 // then the topk largest logits with ties to the lower expert id, each gate the
 // expert's softmax probability (not renormalized).  Lane l holds experts
-// l, l + 64, ...; the max, the sum and every arg-max are xor-butterfly
-// reductions, which leave bit-identical results in all lanes.
+// l, l + 64, ...; the max, the sum and every arg-max are the wave reductions
+// above, which leave bit-identical results in all lanes.
 constexpr int kRouterPer = kMaxExperts / 64;
 
 __device__ inline void route_one_token(const float *row, int32_t n_experts, int32_t topk,
@@ -43,14 +101,12 @@ __device__ inline void route_one_token(const float *row, int32_t n_experts, int3
     v[i] = e < n_experts ? row[e] : -__builtin_inff();
     mx = fmaxf(mx, v[i]);
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+  mx = wave_reduce(mx, [](float a, float b) { return fmaxf(a, b); });
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < kRouterPer; ++i)
     if (lane + 64 * i < n_experts) sum += expf(v[i] - mx);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+  sum = wave_reduce(sum, [](float a, float b) { return a + b; });
   uint32_t taken = 0;
   for (int j = 0; j < topk; ++j) {
     float bv = -__builtin_inff();
@@ -58,20 +114,9 @@ __device__ inline void route_one_token(const float *row, int32_t n_experts, int3
 #pragma unroll
     for (int i = 0; i < kRouterPer; ++i) {
       const int e = lane + 64 * i;
-      if (e < n_experts && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
+      if (e < n_experts && !((taken >> i) & 1u)) better_pair(bv, bi, v[i], e);
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d);
-      const int oi = __shfl_xor(bi, d);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);
     if (lane == bi % 64) taken |= 1u << (bi / 64);
     if (lane == 0) {
       ids[j] = bi;
@@ -130,6 +175,21 @@ __device__ inline void scan_over_waves(int32_t (*hist)[kMaxExperts], int32_t n_e
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP moves, with no
+// LDS round trips: shifts by 1, 2, 4 and 8 lanes inside each row of 16
+// lanes, then the last lane of rows 0 and 2 into rows 1 and 3, and the last
+// lane of row 1 into rows 2 and 3.  Lanes whose source lies outside the row
+// add 0.
+__device__ inline int32_t wave_inclusive_scan(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // From the per-expert totals in base[e]: counts, and (by wave 0) exclusive
 // scans of the counts and tile counts over the experts into base, tile_base
 // and offsets, with base[E] = offsets[E] = all valid pairs and
@@ -157,16 +217,8 @@ __device__ inline void scan_experts(int32_t n_experts, int32_t tile_rows, int ti
       sum += c[i];
       tsum += tc[i];
     }
-    int32_t run = sum, trun = tsum;  // inclusive scan over lanes
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int32_t a = __shfl_up(run, d);
-      const int32_t b = __shfl_up(trun, d);
-      if (lane >= d) {
-        run += a;
-        trun += b;
-      }
-    }
+    int32_t run = wave_inclusive_scan(sum);
+    int32_t trun = wave_inclusive_scan(tsum);
     run -= sum;
     trun -= tsum;
 #pragma unroll
