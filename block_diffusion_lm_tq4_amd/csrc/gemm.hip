@@ -69,7 +69,7 @@ struct GemmArgs {
 };
 
 constexpr int kWaves = 4;          // waves per workgroup, side by side along n
-constexpr int kUpWaves16 = 2;      // the same for the MoE up product on 16-row tiles
+constexpr int kUpWaves16 = 1;      // the same for the MoE up product on 16-row tiles
 constexpr int kChunkBytes = 256;   // one fp16 activation row over one chunk (128 k)
 
 __device__ inline uint32_t f16_bits(float f) {
@@ -1023,10 +1023,11 @@ hipError_t dispatch(int msub, int nsub, int waves_m, const GemmArgs &g, dim3 gri
   if (nsub == 2 && waves_m == 1) {
     switch (msub) {
       case 1:
-        // the 16-row up product: two waves per workgroup, so that the few
-        // (tile, column block) pairs of a small-token layer become twice as
-        // many workgroups (measured 1-2 us faster per 16-token layer; the
-        // same for the down product was 4 us slower)
+        // the 16-row up product: one wave (32 columns) per workgroup, so that
+        // the few (tile, column block) pairs of a small-token layer become
+        // four times as many workgroups (measured per 16-token layer: 4
+        // waves 140-142 us, 2 waves 139-140, 1 wave 136-138; 2 waves for
+        // the down product were 4 us slower)
         if (MODE == kMoEUp) return launch_cfg<1, 2, 1, MODE, kUpWaves16>(g, grid, s);
         return launch_cfg<1, 2, 1, MODE>(g, grid, s);
       case 2: return launch_cfg<2, 2, 1, MODE>(g, grid, s);
