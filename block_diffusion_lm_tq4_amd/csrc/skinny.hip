@@ -510,19 +510,20 @@ __global__ __launch_bounds__(kDmaThreads) void skinny_dma_kernel(SkinnyArgs g) {
     // consumers w and w + kSimds share one, and whole chunks dealt round
     // robin give every SIMD the same share.  What the consumers still have to
     // do once the last chunk is in is the kernel's tail, so the last chunks
-    // are cut finer: each chunk of the last full round of kSimds chunks is
-    // split in halves between the two consumers of one SIMD, and the chunks
-    // of a last, partial round (chunks % kSimds of them) by block over
-    // consumers 0 .. kSimds - 1, one on each SIMD: their whole chunks land
-    // first, so they are the ones done first (measured: the kernel's
-    // consumers w >= kSimds finish about 1 us after the others otherwise).
+    // are cut finer: each chunk of the last two full rounds of kSimds
+    // chunks is split in halves between the two consumers of one SIMD
+    // (measured at K=2688: one round 6.84-6.88 us, two 6.79, three 6.94,
+    // every chunk 6.99), and the chunks of a last, partial round (chunks %
+    // kSimds of them) by block over consumers 0 .. kSimds - 1, one on each
+    // SIMD: their whole chunks land first, so they are the ones done first
+    // (measured: the kernel's consumers w >= kSimds finish about 1 us after
+    // the others otherwise).
     const int full = chunks - chunks % kSimds;
-    const int last = full >= kSimds ? full - kSimds : 0;
+    const int last = full >= 2 * kSimds ? full - 2 * kSimds : 0;
     for (int c = wave; c < last; c += kDmaConsumers)
       default_blocks(std::integral_constant<int, 4>{}, c, 0);
-    if (full >= kSimds)
-      default_blocks(std::integral_constant<int, 2>{}, last + wave % kSimds,
-                     wave < kSimds ? 0 : 2);
+    for (int c = last + wave % kSimds; c < full; c += kSimds)
+      default_blocks(std::integral_constant<int, 2>{}, c, wave < kSimds ? 0 : 2);
     if (wave < kSimds)
       for (int c = full; c < chunks; ++c)
         default_blocks(std::integral_constant<int, 1>{}, c, wave);
