@@ -147,15 +147,33 @@ static_assert(kRouteChunkMin >= kMaxExperts, "a chunk's range of inv holds its c
 
 // Adds the expert counts of pairs [p_begin, p_end) into hist_w (LDS) and
 // returns the number of this lane's pairs whose id is outside [0, n_experts).
+// Batches of 64 ids loaded back to back before any is used, so that a wave
+// waits for one memory latency per group rather than per batch.
+constexpr int kIdBatches = 4;
+
+__device__ inline void load_ids(const int32_t *ids, int64_t p0, int64_t p_end, int lane,
+                                int (&e)[kIdBatches]) {
+#pragma unroll
+  for (int u = 0; u < kIdBatches; ++u) {
+    const int64_t p = p0 + 64 * u + lane;
+    e[u] = (p < p_end) ? ids[p] : -1;
+  }
+}
+
 __device__ inline int32_t count_pairs(const int32_t *ids, int64_t p_begin, int64_t p_end,
                                       int lane, int32_t n_experts, int32_t *hist_w) {
   int32_t bad = 0;
-  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
-    const int64_t p = p0 + lane;
-    const int e = (p < p_end) ? ids[p] : -1;
-    const bool valid = (p < p_end) && e >= 0 && e < n_experts;
-    if (valid) atomicAdd(&hist_w[e], 1);
-    if (p < p_end && !valid) ++bad;
+  for (int64_t g0 = p_begin; g0 < p_end; g0 += 64 * kIdBatches) {
+    int eb[kIdBatches];
+    load_ids(ids, g0, p_end, lane, eb);
+#pragma unroll
+    for (int u = 0; u < kIdBatches; ++u) {
+      const int64_t p = g0 + 64 * u + lane;
+      const int e = eb[u];
+      const bool valid = (p < p_end) && e >= 0 && e < n_experts;
+      if (valid) atomicAdd(&hist_w[e], 1);
+      if (p < p_end && !valid) ++bad;
+    }
   }
   return bad;
 }
@@ -250,23 +268,28 @@ __device__ inline void scatter_pairs(const int32_t *ids, int64_t p_begin, int64_
                                      const int32_t *base, int32_t *hist_w, int32_t *perm,
                                      int32_t *inv) {
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
-    const int64_t p = p0 + lane;
-    const int e = (p < p_end) ? ids[p] : -1;
-    const bool valid = (p < p_end) && e >= 0 && e < n_experts;
-    const uint64_t active = __ballot(valid);
-    const int key = valid ? e : 0;
-    const uint64_t same = same_key_lanes(key, active, key_bits);
-    if (valid) {
-      const int rank = __popcll(same & below);
-      const int32_t slot = base[e] + hist_w[e] + rank;
-      perm[slot] = static_cast<int32_t>(p);
-      inv[p] = slot;
-    } else if (p < p_end) {
-      inv[p] = -1;
+  for (int64_t g0 = p_begin; g0 < p_end; g0 += 64 * kIdBatches) {
+    int eb[kIdBatches];
+    load_ids(ids, g0, p_end, lane, eb);
+#pragma unroll
+    for (int u = 0; u < kIdBatches; ++u) {
+      const int64_t p = g0 + 64 * u + lane;
+      const int e = eb[u];
+      const bool valid = (p < p_end) && e >= 0 && e < n_experts;
+      const uint64_t active = __ballot(valid);
+      const int key = valid ? e : 0;
+      const uint64_t same = same_key_lanes(key, active, key_bits);
+      if (valid) {
+        const int rank = __popcll(same & below);
+        const int32_t slot = base[e] + hist_w[e] + rank;
+        perm[slot] = static_cast<int32_t>(p);
+        inv[p] = slot;
+      } else if (p < p_end) {
+        inv[p] = -1;
+      }
+      // the lowest lane of each key group advances the wave's running count
+      if (valid && (same & below) == 0) hist_w[e] += __popcll(same);
     }
-    // the lowest lane of each key group advances the wave's running count
-    if (valid && (same & below) == 0) hist_w[e] += __popcll(same);
   }
 }
 
