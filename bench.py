@@ -235,10 +235,18 @@ def moe_leg(torch, np, ops, I, wl, experts, steps, warmup, dev, sb, fp8=None):
                       dtype=torch.uint8, device=dev)
     ms_block = time_loop(torch, lambda i: ops.moe_block(x, lg, wl.topk, experts[0], experts[1], sb,
                                                         out=out, workspace=wsb), steps, warmup)
+    # the same block as one persistent launch (tq4_moe_block_persistent), where
+    # its 16-row tiles apply
+    ms_persistent = None
+    wsp_bytes = ops.moe_block_persistent_workspace_size(wl.t, wl.topk, wl.n_experts, wl.n1, wl.k)
+    if wsp_bytes > 0:
+        wsp = torch.zeros(wsp_bytes, dtype=torch.uint8, device=dev)
+        ms_persistent = time_loop(torch, lambda i: ops.moe_block_persistent(
+            x, lg, wl.topk, experts[0], experts[1], sb, out=out, workspace=wsp), steps, warmup)
     touched = np.unique(ids).size
     per_expert = (wl.n1 * (wl.k // 32) + wl.k * (wl.n1 // 32)) * 20
     pairs = wl.t * wl.topk
-    r = dict(ms_step=ms, ms_router=ms_router, ms_block=ms_block,
+    r = dict(ms_step=ms, ms_router=ms_router, ms_block=ms_block, ms_persistent=ms_persistent,
              packed_bytes=touched * per_expert,
              flops=2.0 * pairs * 2 * wl.n1 * wl.k, experts_touched=int(touched))
     if fp8 is not None:
@@ -725,6 +733,8 @@ def main() -> int:
                           "TFLOP/s": round(tf, 2), "experts_touched": q["experts_touched"],
                           "router_us": round(q["ms_router"] * 1e3, 2),
                           "block_from_logits_us": round(q["ms_block"] * 1e3, 2),
+                          "block_persistent_us": (None if q["ms_persistent"] is None else
+                                                  round(q["ms_persistent"] * 1e3, 2)),
                           "roofline": {"bound": "hbm", "achieved": round(g2, 1),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": round(g2 / HBM_PEAK_GBS, 4)},

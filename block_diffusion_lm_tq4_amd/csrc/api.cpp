@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "../../include/tq4.h"
+#include "moe_block.h"
 #include "tq4_internal.h"
 
 namespace {
@@ -404,6 +405,50 @@ int tq4_moe_block(const uint16_t *x_bf16, int64_t t, int64_t k, const float *log
     e = moe_layer(x_bf16, t, k, ids, gates, topk, n_experts, w1_packed, n1, w2_packed, sign_bits,
                   out, ws, s);
   return device_status(e);
+}
+
+size_t tq4_moe_block_persistent_workspace_size(int64_t t, int32_t topk, int32_t n_experts,
+                                               int64_t n1, int64_t k) {
+  const size_t blk = tq4_moe_block_workspace_size(t, topk, n_experts, n1, k);
+  if (blk == 0 || tq4::plan_moe(t * topk, n_experts).msub != 1) return 0;
+  return blk + align_up(tq4::moe_block_persistent_scratch_bytes());
+}
+
+int tq4_moe_block_persistent(const uint16_t *x_bf16, int64_t t, int64_t k, const float *logits,
+                             int32_t n_experts, int32_t topk, const uint8_t *w1_packed,
+                             int64_t n1, const uint8_t *w2_packed, uint32_t sign_bits,
+                             float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!moe_shape_ok(t, topk, n_experts, n1, k)) return TQ4_E_SHAPE;
+  const MoEPlan p = tq4::plan_moe(t * topk, n_experts);
+  if (p.msub != 1) return TQ4_E_SHAPE;
+  if (t == 0) return TQ4_OK;
+  if (logits == nullptr) return TQ4_E_NULL;
+  const int st = moe_args_status(x_bf16, w1_packed, w2_packed, out);
+  if (st != TQ4_OK) return st;
+  if (!aligned(logits, 4)) return TQ4_E_ALIGN;
+  const size_t need = tq4_moe_block_persistent_workspace_size(t, topk, n_experts, n1, k);
+  if (workspace == nullptr || workspace_bytes < need) return TQ4_E_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return TQ4_E_ALIGN;
+  char *ws = static_cast<char *>(workspace);
+  const MoELayout l = moe_layout(t, topk, n_experts, n1, k, p);
+  const size_t slots = static_cast<size_t>(t) * static_cast<size_t>(topk);
+  tq4::MoEScratch sc{};
+  sc.counts = reinterpret_cast<int32_t *>(ws + l.counts);
+  sc.offsets = reinterpret_cast<int32_t *>(ws + l.offsets);
+  sc.perm = reinterpret_cast<int32_t *>(ws + l.perm);
+  sc.inv = reinterpret_cast<int32_t *>(ws + l.inv);
+  sc.tiles = reinterpret_cast<MoETile *>(ws + l.tiles);
+  sc.n_tiles = reinterpret_cast<int32_t *>(ws + l.meta);
+  sc.xt = reinterpret_cast<uint16_t *>(ws + l.xt);
+  sc.ht = reinterpret_cast<uint16_t *>(ws + l.ht);
+  sc.o = reinterpret_cast<float *>(ws + l.o);
+  sc.ids = reinterpret_cast<int32_t *>(ws + l.total);
+  sc.gates = reinterpret_cast<float *>(ws + l.total + align_up(slots * sizeof(int32_t)));
+  sc.bar = reinterpret_cast<uint32_t *>(ws + l.total + align_up(slots * sizeof(int32_t)) +
+                                        align_up(slots * sizeof(float)));
+  return device_status(tq4::launch_moe_block_persistent(x_bf16, t, k, logits, n_experts, topk,
+                                                        w1_packed, n1, w2_packed, sign_bits, out,
+                                                        sc, as_stream(stream)));
 }
 
 // ---- fp8 weight cache ---------------------------------------------------

@@ -36,6 +36,7 @@
 // rows and stores acc with both shifts undone.  Tiles past the device-side count exit at once, so the
 // grid is sized on the host from t*topk without a sync.
 #include "tq4_internal.h"
+#include "moe_block.h"
 
 namespace tq4 {
 namespace {
@@ -45,6 +46,8 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
+
+#include "moe_route.h"
 
 enum Mode { kDense = 0, kMoEUp = 1, kMoEDown = 2 };
 
@@ -200,9 +203,8 @@ struct WRaw {
 // rows, and a popular expert, whose tiles are consecutive, is spread evenly
 // over the XCDs and read about once by each of them.  Returns false for
 // workgroups past the device-side tile count.
-__device__ inline bool moe_item(const GemmArgs &g, int &tile, int64_t &col_block) {
+__device__ inline bool moe_item(const GemmArgs &g, int lin, int &tile, int64_t &col_block) {
   const int cols = g.tiles_n;
-  const int lin = static_cast<int>(blockIdx.x);
   const int j = lin / 8;
   tile = 8 * (j / cols) + lin % 8;
   col_block = j % cols;
@@ -334,21 +336,18 @@ __device__ inline void moe_store(const floatx4 (&acc)[MSUB][NSUB], const GemmArg
 // layer at 16 and 1024 tokens).
 constexpr int waves_per_eu_for(int msub) { return msub == 1 ? 6 : (msub == 4 ? 4 : 1); }
 
-template <int MSUB, int NSUB, int LUTC, int MODE, int WV = kWaves>
-__global__ __launch_bounds__(64 * WV)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(GemmArgs g) {
+// One workgroup tile of the product: `lin` is the tile's linear index (the
+// workgroup id of gemm_kernel), `split_z` its K range (dense split-K); abuf0
+// and abuf1 are the activation stages (16 * MSUB * kChunkBytes bytes each,
+// 16-byte aligned) and lut the pair table (256 * LUTC words), all LDS.
+// Every thread of the workgroup calls it (it holds workgroup barriers).
+template <int MSUB, int NSUB, int LUTC, int MODE, int WV>
+__device__ inline void gemm_tile(const GemmArgs &g, int lin, int split_z, uint8_t *abuf0,
+                                 uint8_t *abuf1, uint32_t *lut) {
   constexpr int TM = 16 * MSUB;           // activation rows per workgroup
   constexpr int TN = 16 * NSUB * WV;      // weight rows per workgroup
   constexpr int LPW = 4 * MSUB / WV;      // activation loads per wave per chunk
   static_assert(LPW * WV == 4 * MSUB, "activation loads split evenly");
-
-  // Activation tile of one chunk, double buffered.  Row r occupies 256 bytes
-  // (16 slots of 8 halves); global slot s of row r is stored in slot
-  // s ^ (r % 16), so the fragment reads below (16 rows, one slot each) fall
-  // on 16 distinct 16-byte bank groups.
-  __shared__ __attribute__((aligned(16))) uint8_t abuf0[TM * kChunkBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t abuf1[TM * kChunkBytes];
-  __shared__ uint32_t lut[256 * LUTC];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
@@ -367,16 +366,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
     // renumber so that each XCD works on a contiguous range of tiles (a band
     // of activation rows against all weight rows), which its own L2 serves.
     const int tiles = g.tiles_m * g.tiles_n;
-    int t = static_cast<int>(blockIdx.x);
+    int t = lin;
     if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
     m_base = static_cast<int64_t>(t / g.tiles_n) * TM;
     n_base = static_cast<int64_t>(t % g.tiles_n) * TN;
     rows_valid = g.m - m_base;
-    split = blockIdx.z;
+    split = split_z;
   } else {
     int ti;
     int64_t cb;
-    if (!moe_item(g, ti, cb)) return;
+    if (!moe_item(g, lin, ti, cb)) return;
     const MoETile t = g.tiles[ti];
     m_base = t.row0;
     rows_valid = t.rows;
@@ -529,6 +528,20 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
     static_assert(WV * 8 * MSUB * 32 * 4 <= TM * kChunkBytes, "staging fits");
     moe_store<MSUB, NSUB, MODE>(acc, g, m_base, rows_valid, n_base, wave, lane, abuf0, abuf1);
   }
+}
+
+template <int MSUB, int NSUB, int LUTC, int MODE, int WV = kWaves>
+__global__ __launch_bounds__(64 * WV)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(GemmArgs g) {
+  // Activation tile of one chunk, double buffered.  Row r occupies 256 bytes
+  // (16 slots of 8 halves); global slot s of row r is stored in slot
+  // s ^ (r % 16), so the fragment reads (16 rows, one slot each) fall on 16
+  // distinct 16-byte bank groups.
+  __shared__ __attribute__((aligned(16))) uint8_t abuf0[16 * MSUB * kChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf1[16 * MSUB * kChunkBytes];
+  __shared__ uint32_t lut[256 * LUTC];
+  gemm_tile<MSUB, NSUB, LUTC, MODE, WV>(g, static_cast<int>(blockIdx.x),
+                                        static_cast<int>(blockIdx.z), abuf0, abuf1, lut);
 }
 
 // Dense large-M variant of the same product, software-pipelined by k-step.
@@ -1052,6 +1065,153 @@ hipError_t dispatch(int msub, int nsub, int waves_m, const GemmArgs &g, dim3 gri
   return hipErrorInvalidValue;
 }
 
+
+// ---------------------------------------------------------------------------
+// The MoE block in one persistent launch (Nemotron-TheHobbit-30B-A3B model
+// card: section Running it, "sync-free MoE", and the help-wanted list's
+// fused kernels).  A cooperative launch of as many 4-wave workgroups as the
+// device holds at once (4 per compute unit) runs the block's steps in order,
+// with a grid-wide barrier between steps:
+//   1. workgroup 0 routes every token (route_one_token, one wave per token)
+//      and buckets the pairs (bucket_group), as the bucketing launch of
+//      tq4_moe_block does; the other workgroups rotate the activation rows
+//      (one thread per 32-block);
+//   2. the up product, ReLU^2 and the rotation of the hidden rows, one
+//      (16-row tile, 128-column block) per workgroup and item (gemm_tile);
+//   3. the down product, likewise;
+//   4. the weighted combine (combine_quad), four outputs per thread.
+// Each step is the code of the launch that does it in tq4_moe_block, on
+// the same data in the same order, so the results are the same bit for bit.
+// Items are dealt as gemm_kernel's grid deals its workgroups (moe_item), the
+// grid being a multiple of 8 workgroups, so an item runs on the XCD that
+// workgroup would have.  The 16-token layer's items (about 1100 and 1500)
+// take two rounds each on the 1024 workgroups.  One round would need 6
+// workgroups per compute unit, i.e. at most 80 registers per lane: the
+// compiler then spills, and a reload ahead of the chunk loop makes it wait
+// for every load in flight on each chunk, which costs more than the second
+// round (measured at 16 tokens: 362 against 275 us per call).
+//
+// The barrier: after a workgroup barrier one thread of each workgroup
+// releases the workgroup's writes (an agent-scope fence, which writes them
+// back to memory before it returns) and counts itself in one of kBarStripes
+// counters, 128-byte lines apart; the last of a stripe counts the stripe in
+// a top counter, and the last stripe writes the round into kBarFlags flag
+// words.  The waiting workgroups poll one flag each (one lane, spread over
+// the flags), then acquire (an agent-scope fence: their caches no longer
+// hold lines from before).  Counters only grow within a launch (round r
+// completes at r arrivals per workgroup); a small kernel zeroes them before
+// it.  A poll gives up after kBarSpinLimit rounds, so a grid that could not
+// be co-resident ends with wrong results instead of hanging (the
+// cooperative launch refuses such grids anyway).
+constexpr int kBlockWaves = 4;
+constexpr int kBlockThreads = 64 * kBlockWaves;
+constexpr int kBarStripes = 16;
+constexpr int kBarFlags = 32;
+constexpr int kBarStride = 32;  // words: one counter or flag per 128-byte line
+constexpr int kBarWords = (kBarStripes + 1 + kBarFlags) * kBarStride;
+constexpr uint32_t kBarSpinLimit = 1u << 20;
+
+struct BlockArgs {
+  GemmArgs up, down;  // the grouped products; tiles_n = 128-column blocks
+  const float *logits;
+  const uint16_t *x;
+  int64_t t, k, x_blocks;
+  int32_t n_experts, topk, tile_rows;
+  uint32_t sign_bits;
+  int32_t *ids;
+  float *gates;
+  int32_t *counts, *offsets, *perm, *inv;
+  MoETile *tiles;
+  int32_t *n_tiles;
+  uint16_t *xt;
+  float *o, *out;
+  uint32_t *bar;  // kBarWords words, zero at the start
+};
+
+__device__ inline void grid_barrier(uint32_t *bar, uint32_t round) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t nblk = gridDim.x;
+    const uint32_t s = blockIdx.x % kBarStripes;
+    const uint32_t stripes = nblk < kBarStripes ? nblk : kBarStripes;
+    const uint32_t per = (nblk - s + kBarStripes - 1) / kBarStripes;  // workgroups of stripe s
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t old = __hip_atomic_fetch_add(bar + s * kBarStride, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == round * per &&
+        __hip_atomic_fetch_add(bar + kBarStripes * kBarStride, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) + 1 == round * stripes) {
+      for (int c = 0; c < kBarFlags; ++c)
+        __hip_atomic_store(bar + (kBarStripes + 1 + c) * kBarStride, round, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint32_t *flag = bar + (kBarStripes + 1 + blockIdx.x % kBarFlags) * kBarStride;
+    for (uint32_t spin = 0; spin < kBarSpinLimit; ++spin) {
+      if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= round) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kBlockThreads) void moe_block_kernel(BlockArgs b) {
+  __shared__ __attribute__((aligned(16))) uint8_t abuf0[16 * kChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf1[16 * kChunkBytes];
+  __shared__ uint32_t lut[256];
+  __shared__ int32_t hist[kBlockWaves][kMaxExperts];
+  __shared__ int32_t base[kMaxExperts + 1];
+  __shared__ int32_t tile_base[kMaxExperts + 1];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int64_t nblk = gridDim.x;
+  const int64_t blk = blockIdx.x;
+
+  // 1. routing and bucketing (workgroup 0), activation rotation (the rest)
+  if (blk == 0) {
+    for (int64_t tok = wave; tok < b.t; tok += kBlockWaves)
+      route_one_token(b.logits + tok * b.n_experts, b.n_experts, b.topk, lane,
+                      b.ids + tok * b.topk, b.gates + tok * b.topk);
+    // the ids are read back by this workgroup only
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __syncthreads();
+    bucket_group<kBlockWaves>(hist, base, tile_base, b.ids, b.t * b.topk, b.n_experts, b.counts,
+                              b.offsets, b.perm, b.inv, b.tiles, b.n_tiles, b.tile_rows,
+                              nullptr);
+  } else {
+    for (int64_t i = (blk - 1) * kBlockThreads + tid; i < b.x_blocks;
+         i += (nblk - 1) * kBlockThreads)
+      rotate_block_bf16(b.x + i * 32, b.sign_bits, b.xt + i * 32);
+  }
+  grid_barrier(b.bar, 1);
+
+  // 2, 3. the grouped products; a workgroup barrier after each item, since
+  // the next one's loads refill stages the up epilogue may still be reading
+  const int64_t tiles8 = (static_cast<int64_t>(*b.n_tiles) + 7) / 8 * 8;
+  for (int64_t it = blk; it < tiles8 * b.up.tiles_n; it += nblk) {
+    gemm_tile<1, 2, 1, kMoEUp, kBlockWaves>(b.up, static_cast<int>(it), 0, abuf0, abuf1, lut);
+    __syncthreads();
+  }
+  grid_barrier(b.bar, 2);
+  for (int64_t it = blk; it < tiles8 * b.down.tiles_n; it += nblk) {
+    gemm_tile<1, 2, 1, kMoEDown, kBlockWaves>(b.down, static_cast<int>(it), 0, abuf0, abuf1,
+                                              lut);
+    __syncthreads();
+  }
+  grid_barrier(b.bar, 3);
+
+  // 4. combine
+  const int64_t q = b.k / 4;
+  for (int64_t i = blk * kBlockThreads + tid; i < b.t * q; i += nblk * kBlockThreads)
+    combine_quad(b.o, b.inv, b.gates, i / q, i % q, b.topk, b.k, b.out);
+}
+
+__global__ __launch_bounds__(256) void bar_reset_kernel(uint32_t *bar) {
+  for (int i = threadIdx.x; i < kBarWords; i += 256) bar[i] = 0u;
+}
+
 }  // namespace
 
 DensePlan plan_dense(int64_t m, int64_t k, int64_t n) {
@@ -1154,11 +1314,13 @@ MoEPlan plan_moe(int64_t pairs, int32_t n_experts) {
   return p;
 }
 
-hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_t k,
-                           const int32_t *perm, int32_t topk, const uint8_t *w_packed, int64_t n,
-                           const MoETile *tiles, const int32_t *n_tiles, float *out,
-                           uint16_t *out16, uint32_t sign_bits, hipStream_t s) {
-  if (mode == 0 && n % 32 != 0) return hipErrorInvalidValue;
+namespace {
+
+// Arguments of a grouped product over the MoE tile list; tiles_n (the column
+// blocks) is set by the caller from its workgroup width.
+GemmArgs moe_gemm_args(const uint16_t *a, int64_t k, const int32_t *perm, int32_t topk,
+                       const uint8_t *w_packed, int64_t n, const MoETile *tiles,
+                       const int32_t *n_tiles, float *out, uint16_t *out16, uint32_t sign_bits) {
   GemmArgs g{};
   g.a = a;
   g.w = w_packed;
@@ -1176,6 +1338,17 @@ hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_
   g.ksplit = 1;
   g.chunks = static_cast<int32_t>((k / 32 + 3) / 4);
   g.cb = codebook();
+  return g;
+}
+
+}  // namespace
+
+hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_t k,
+                           const int32_t *perm, int32_t topk, const uint8_t *w_packed, int64_t n,
+                           const MoETile *tiles, const int32_t *n_tiles, float *out,
+                           uint16_t *out16, uint32_t sign_bits, hipStream_t s) {
+  if (mode == 0 && n % 32 != 0) return hipErrorInvalidValue;
+  GemmArgs g = moe_gemm_args(a, k, perm, topk, w_packed, n, tiles, n_tiles, out, out16, sign_bits);
   // one workgroup per (tile, column block) pair that can exist, the tile
   // count rounded up to a multiple of 8 (see moe_item)
   const int64_t wg_n = 16 * p.nsub * (mode == 0 && p.msub == 1 ? kUpWaves16 : p.waves_n);
@@ -1184,6 +1357,70 @@ hipError_t launch_moe_gemm(const MoEPlan &p, int mode, const uint16_t *a, int64_
   const dim3 grid(static_cast<unsigned>((p.max_tiles + 7) / 8 * 8 * cols), 1, 1);
   if (mode == 0) return dispatch<kMoEUp>(p.msub, p.nsub, p.waves_m, g, grid, s);
   return dispatch<kMoEDown>(p.msub, p.nsub, p.waves_m, g, grid, s);
+}
+
+
+size_t moe_block_persistent_scratch_bytes() { return kBarWords * sizeof(uint32_t); }
+
+hipError_t launch_moe_block_persistent(const uint16_t *x, int64_t t, int64_t k,
+                                       const float *logits, int32_t n_experts, int32_t topk,
+                                       const uint8_t *w1, int64_t n1, const uint8_t *w2,
+                                       uint32_t sign_bits, float *out, const MoEScratch &sc,
+                                       hipStream_t s) {
+  const MoEPlan p = plan_moe(t * topk, n_experts);
+  if (p.msub != 1 || n1 % 32 != 0 || k % 4 != 0 || n_experts > kMaxExperts)
+    return hipErrorInvalidValue;
+  // co-resident workgroups of this device, a multiple of 8 (cached per device)
+  static int grid_of[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (grid_of[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_block_kernel, kBlockThreads, 0);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int g = per_cu * cus / 8 * 8;
+    if (g < 8) return hipErrorInvalidConfiguration;
+    grid_of[dev] = g;
+  }
+  BlockArgs b{};
+  b.up = moe_gemm_args(sc.xt, k, sc.perm, topk, w1, n1, sc.tiles, sc.n_tiles, nullptr, sc.ht,
+                       sign_bits);
+  b.down = moe_gemm_args(sc.ht, n1, sc.perm, topk, w2, k, sc.tiles, sc.n_tiles, sc.o, nullptr,
+                         sign_bits);
+  const int64_t wg_n = 16 * 2 * kBlockWaves;
+  b.up.tiles_n = static_cast<int32_t>((n1 + wg_n - 1) / wg_n);
+  b.down.tiles_n = static_cast<int32_t>((k + wg_n - 1) / wg_n);
+  b.logits = logits;
+  b.x = x;
+  b.t = t;
+  b.k = k;
+  b.x_blocks = t * (k / 32);
+  b.n_experts = n_experts;
+  b.topk = topk;
+  b.tile_rows = p.tile_rows;
+  b.sign_bits = sign_bits;
+  b.ids = sc.ids;
+  b.gates = sc.gates;
+  b.counts = sc.counts;
+  b.offsets = sc.offsets;
+  b.perm = sc.perm;
+  b.inv = sc.inv;
+  b.tiles = sc.tiles;
+  b.n_tiles = sc.n_tiles;
+  b.xt = sc.xt;
+  b.o = sc.o;
+  b.out = out;
+  b.bar = sc.bar;
+  hipLaunchKernelGGL(bar_reset_kernel, dim3(1), dim3(256), 0, s, sc.bar);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  void *args[] = {&b};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(moe_block_kernel),
+                                    dim3(static_cast<unsigned>(grid_of[dev])),
+                                    dim3(kBlockThreads), args, 0, s);
 }
 
 }  // namespace tq4

@@ -467,6 +467,40 @@ def moe_block(x: torch.Tensor, logits: torch.Tensor, topk: int, w1_packed: torch
     return out
 
 
+def moe_block_persistent_workspace_size(t: int, topk: int, n_experts: int, n1: int,
+                                        k: int) -> int:
+    return int(lib().tq4_moe_block_persistent_workspace_size(t, topk, n_experts, n1, k))
+
+
+def moe_block_persistent(x: torch.Tensor, logits: torch.Tensor, topk: int,
+                         w1_packed: torch.Tensor, w2_packed: torch.Tensor, sign_bits: int,
+                         out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_block in one persistent launch (tq4_moe_block_persistent); 16-row tiles only."""
+    _cuda_contig(x, "x", torch.bfloat16)
+    _cuda_contig(logits, "logits", torch.float32)
+    _cuda_contig(w1_packed, "w1_packed", torch.uint8)
+    _cuda_contig(w2_packed, "w2_packed", torch.uint8)
+    t, k = x.shape
+    e, n1, kb1, bb = w1_packed.shape
+    _require(tuple(logits.shape) == (t, e), "logits must be [t, E]")
+    _require(kb1 * BLOCK == k and bb == BLOCK_BYTES, "w1_packed must be [E, n1, k/32, 20]")
+    _require(tuple(w2_packed.shape) == (e, k, n1 // BLOCK, BLOCK_BYTES),
+             "w2_packed must be [E, k, n1/32, 20]")
+    if out is None:
+        out = torch.empty((t, k), dtype=torch.float32, device=x.device)
+    _cuda_contig(out, "out", torch.float32)
+    need = moe_block_persistent_workspace_size(t, topk, e, n1, k)
+    _require(need > 0, "sizes outside tq4_moe_block_persistent's range")
+    if workspace is None:
+        workspace = _WS.get(x.device, "moe_block_persistent", need)
+    check("tq4_moe_block_persistent", lib().tq4_moe_block_persistent(
+        x.data_ptr(), t, k, logits.data_ptr(), e, topk, w1_packed.data_ptr(), n1,
+        w2_packed.data_ptr(), sign_bits & 0xFFFFFFFF, out.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream(x.device)))
+    return out
+
+
 def read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
     """One streaming read of a whole device buffer (tq4_read_probe), for timing."""
     _require(buf.is_cuda and buf.is_contiguous(), "buf must be a contiguous device tensor")

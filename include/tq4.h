@@ -396,6 +396,28 @@ int tq4_moe_block(const uint16_t *x_bf16, int64_t t, int64_t k, const float *log
                   const uint8_t *w2_packed, uint32_t sign_bits, float *out, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/* Workspace bytes tq4_moe_block_persistent needs (0 if the sizes are
+ * invalid or outside its range). */
+size_t tq4_moe_block_persistent_workspace_size(int64_t t, int32_t topk, int32_t n_experts,
+                                               int64_t n1, int64_t k);
+
+/* tq4_moe_block as one persistent kernel (model card, Running it: sync-free
+ * MoE; the help-wanted list asks for fused kernels): a small launch that
+ * clears the grid barrier's counters, then one cooperative launch of as many
+ * workgroups as the device holds at once, which runs the router, the
+ * activation rotation, the bucketing, the up product with ReLU^2, the down
+ * product and the weighted combine in that order, with a grid-wide barrier
+ * between them.  Results equal tq4_moe_block's bit for bit.  Only for
+ * layers whose tiles are 16 rows: t * topk <= 16 * n_experts (a denoiser
+ * block of 16 tokens is 96 pairs).  Not graph-capturable (a cooperative
+ * launch).  Arguments as tq4_moe_block; workspace of at least
+ * tq4_moe_block_persistent_workspace_size(...) bytes, 256-byte aligned.
+ * Errors as tq4_moe_block; TQ4_E_SHAPE also for t * topk > 16 * n_experts. */
+int tq4_moe_block_persistent(const uint16_t *x_bf16, int64_t t, int64_t k, const float *logits,
+                             int32_t n_experts, int32_t topk, const uint8_t *w1_packed,
+                             int64_t n1, const uint8_t *w2_packed, uint32_t sign_bits,
+                             float *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Measurement aid: the same layer computed with another placement of the
  * rotation or another arithmetic for the product, so that the library's
  * choice can be measured against the alternatives the format admits (model

@@ -277,6 +277,34 @@ def test_moe_block_argument_errors(L):
     assert call(t=0) == OK
 
 
+def test_moe_block_persistent_argument_errors(L):
+    ws = L.tq4_moe_block_persistent_workspace_size(16, 6, 128, 1856, 2688)
+    assert ws > L.tq4_moe_block_workspace_size(16, 6, 128, 1856, 2688)
+    # 16-row tiles only: t * topk <= 16 * n_experts
+    assert L.tq4_moe_block_persistent_workspace_size(341, 6, 128, 1856, 2688) > 0
+    assert L.tq4_moe_block_persistent_workspace_size(342, 6, 128, 1856, 2688) == 0
+    assert L.tq4_moe_block_persistent_workspace_size(16, 6, 128, 1850, 2688) == 0
+
+    def call(**kw):
+        a = dict(dict(x=FAKE, t=16, k=2688, lg=FAKE, e=128, topk=6, w1=FAKE, n1=1856, w2=FAKE,
+                      out=FAKE, ws=FAKE, wsb=ws), **kw)
+        return L.tq4_moe_block_persistent(a["x"], a["t"], a["k"], a["lg"], a["e"], a["topk"],
+                                          a["w1"], a["n1"], a["w2"], 0, a["out"], a["ws"],
+                                          a["wsb"], None)
+
+    assert call(t=342) == E_SHAPE
+    assert call(topk=129) == E_SHAPE
+    assert call(e=513) == E_SHAPE
+    assert call(n1=1850) == E_SHAPE
+    assert call(lg=None) == E_NULL
+    assert call(w2=None) == E_NULL
+    assert call(lg=FAKE + 2) == E_ALIGN
+    assert call(out=MIS) == E_ALIGN
+    assert call(ws=None) == E_WS
+    assert call(wsb=ws - 1) == E_WS
+    assert call(t=0) == OK
+
+
 def test_moe_grouped_fp8_argument_errors(L):
     ws = L.tq4_moe_grouped_fp8_workspace_size(16, 6, 128, 1856, 2688)
     # route lists, 16-row tiles, xq/xs (kp 2688), hq/hs (n1p 1920), fp32 o

@@ -635,6 +635,59 @@ def test_moe_block_router_placements(dev, t, e, topk):
                  f"moe block t{t} e{e} top{topk}")
 
 
+def test_moe_block_persistent_t16_equals_moe_block(dev, experts):
+    """tq4_moe_block_persistent on the 16-token block of the 128-expert layer:
+    the same bits as tq4_moe_block (each of its steps runs the code of the
+    corresponding launch on the same data), twice on one workspace (the grid
+    barrier's counters are cleared per call), and the oracle's router + layer
+    on every token."""
+    wl = I.WORKLOADS["moe_t16"]
+    lg = I.router_logits(wl.t, wl.n_experts, "uniform", seed=9).astype(np.float32)
+    x_bits = I.activations_bf16(wl.t, wl.k, seed=10)
+    xb = _bf16(x_bits, dev)
+    lg_d = torch.from_numpy(lg).to(dev)
+    out = _ops().moe_block_persistent(xb, lg_d, wl.topk, experts[0], experts[1], SB).clone()
+    again = _ops().moe_block_persistent(xb, lg_d, wl.topk, experts[0], experts[1], SB)
+    ref = _ops().moe_block(xb, lg_d, wl.topk, experts[0], experts[1], SB)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(again, ref)
+    ref_ids, ref_g = O.router(lg, wl.topk)
+    oracle = O.moe(x_bits, ref_ids, ref_g, _oracle_expert(experts, 1), _oracle_expert(experts, 2),
+                   SB)
+    _check_close(out.cpu().numpy(), oracle, "moe block persistent t16")
+
+
+@pytest.mark.parametrize("t,e,topk", [
+    (1, 8, 2),       # one token, fewer pairs than waves
+    (17, 128, 6),
+    (64, 100, 8),    # experts not a multiple of 64
+    (40, 512, 4),    # the largest expert count
+    (300, 128, 6),   # 1800 pairs: many 16-row tiles per expert
+])
+def test_moe_block_persistent_shapes(dev, t, e, topk):
+    """tq4_moe_block_persistent equals tq4_moe_block bit for bit and matches
+    the oracle's router + layer, over token and expert counts."""
+    rng = np.random.default_rng(t * 7 + e)
+    k, n1 = 96, 64
+    w1 = (0.05 * rng.standard_normal((e, n1, k))).astype(np.float32)
+    w2 = (0.05 * rng.standard_normal((e, k, n1))).astype(np.float32)
+    p1 = np.stack([O.pack(w1[i], SB) for i in range(e)])
+    p2 = np.stack([O.pack(w2[i], SB) for i in range(e)])
+    lg = I.router_logits(t, e, "zipf", seed=t + 3).astype(np.float32)
+    x_bits = I.activations_bf16(t, k, seed=t + 4)
+    xb = _bf16(x_bits, dev)
+    lg_d = torch.from_numpy(lg).to(dev)
+    p1d, p2d = torch.from_numpy(p1).to(dev), torch.from_numpy(p2).to(dev)
+    out = _ops().moe_block_persistent(xb, lg_d, topk, p1d, p2d, SB)
+    ref = _ops().moe_block(xb, lg_d, topk, p1d, p2d, SB)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    ref_ids, ref_g = O.router(lg, topk)
+    _check_close(out.cpu().numpy(), O.moe(x_bits, ref_ids, ref_g, list(p1), list(p2), SB),
+                 f"moe block persistent t{t} e{e} top{topk}")
+
+
 def test_moe_deterministic(dev, experts):
     wl = I.WORKLOADS["moe_t1024_zipf"]
     ids, g = I.moe_routing(wl)
