@@ -1092,13 +1092,13 @@ hipError_t dispatch(int msub, int nsub, int waves_m, const GemmArgs &g, dim3 gri
 // round (measured at 16 tokens: 362 against 275 us per call).
 //
 // The barrier: after a workgroup barrier one thread of each workgroup
-// releases the workgroup's writes (an agent-scope fence, which writes them
-// back to memory before it returns) and counts itself in one of kBarStripes
-// counters, 128-byte lines apart; the last of a stripe counts the stripe in
-// a top counter, and the last stripe writes the round into kBarFlags flag
-// words.  The waiting workgroups poll one flag each (one lane, spread over
-// the flags), then acquire (an agent-scope fence: their caches no longer
-// hold lines from before).  Counters only grow within a launch (round r
+// releases the workgroup's writes (an agent-scope fence) and counts itself
+// in one of kBarStripes counters, 128-byte lines apart; the last of a
+// stripe acquires and re-releases (fence to fence through the counter's
+// chain of adds) and counts the stripe in a top counter, and the last
+// stripe does the same and writes the round into kBarFlags flag words.  The
+// waiting workgroups poll one flag each (one lane, spread over the flags),
+// then acquire.  Counters only grow within a launch (round r
 // completes at r arrivals per workgroup); a small kernel zeroes them before
 // it.  A poll gives up after kBarSpinLimit rounds, so a grid that could not
 // be co-resident ends with wrong results instead of hanging (the
@@ -1138,12 +1138,18 @@ __device__ inline void grid_barrier(uint32_t *bar, uint32_t round) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t old = __hip_atomic_fetch_add(bar + s * kBarStride, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 == round * per &&
-        __hip_atomic_fetch_add(bar + kBarStripes * kBarStride, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT) + 1 == round * stripes) {
-      for (int c = 0; c < kBarFlags; ++c)
-        __hip_atomic_store(bar + (kBarStripes + 1 + c) * kBarStride, round, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == round * per) {
+      // the last of the stripe acquires the stripe's releases (its add read
+      // the end of their chain of adds) and passes them on
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      const uint32_t top = __hip_atomic_fetch_add(bar + kBarStripes * kBarStride, 1u,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (top + 1 == round * stripes) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+        for (int c = 0; c < kBarFlags; ++c)
+          __hip_atomic_store(bar + (kBarStripes + 1 + c) * kBarStride, round, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     const uint32_t *flag = bar + (kBarStripes + 1 + blockIdx.x % kBarFlags) * kBarStride;
     for (uint32_t spin = 0; spin < kBarSpinLimit; ++spin) {
