@@ -38,6 +38,8 @@
 #include "tq4_internal.h"
 #include "moe_block.h"
 
+#include <atomic>
+
 namespace tq4 {
 namespace {
 
@@ -1376,20 +1378,22 @@ hipError_t launch_moe_block_persistent(const uint16_t *x, int64_t t, int64_t k,
   const MoEPlan p = plan_moe(t * topk, n_experts);
   if (p.msub != 1 || n1 % 32 != 0 || k % 4 != 0 || n_experts > kMaxExperts)
     return hipErrorInvalidValue;
-  // co-resident workgroups of this device, a multiple of 8 (cached per device)
-  static int grid_of[64] = {0};
+  // co-resident workgroups of this device, a multiple of 8 (cached per
+  // device; concurrent first calls compute the same value)
+  static std::atomic<int> grid_of[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (grid_of[dev] == 0) {
+  int grid = grid_of[dev].load(std::memory_order_relaxed);
+  if (grid == 0) {
     int per_cu = 0, cus = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_block_kernel, kBlockThreads, 0);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const int g = per_cu * cus / 8 * 8;
-    if (g < 8) return hipErrorInvalidConfiguration;
-    grid_of[dev] = g;
+    grid = per_cu * cus / 8 * 8;
+    if (grid < 8) return hipErrorInvalidConfiguration;
+    grid_of[dev].store(grid, std::memory_order_relaxed);
   }
   BlockArgs b{};
   b.up = moe_gemm_args(sc.xt, k, sc.perm, topk, w1, n1, sc.tiles, sc.n_tiles, nullptr, sc.ht,
@@ -1425,7 +1429,7 @@ hipError_t launch_moe_block_persistent(const uint16_t *x, int64_t t, int64_t k,
   if (e != hipSuccess) return e;
   void *args[] = {&b};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(moe_block_kernel),
-                                    dim3(static_cast<unsigned>(grid_of[dev])),
+                                    dim3(static_cast<unsigned>(grid)),
                                     dim3(kBlockThreads), args, 0, s);
 }
 
