@@ -341,17 +341,17 @@ constexpr int waves_per_eu_for(int msub) { return msub == 1 ? 6 : (msub == 4 ? 4
 // One workgroup tile of the product: `lin` is the tile's linear index (the
 // workgroup id of gemm_kernel), `split_z` its K range (dense split-K); abuf0
 // and abuf1 are the activation stages (16 * MSUB * kChunkBytes bytes each,
-// 16-byte aligned) and lut the pair table (256 * LUTC words), all LDS.
-// Every thread of the workgroup calls it (it holds workgroup barriers).
+// 16-byte aligned) and lut the pair table (256 * LUTC words), all LDS; tid
+// is the thread's index in the workgroup.  Every thread of the workgroup
+// calls it (it holds workgroup barriers).
 template <int MSUB, int NSUB, int LUTC, int MODE, int WV>
 __device__ inline void gemm_tile(const GemmArgs &g, int lin, int split_z, uint8_t *abuf0,
-                                 uint8_t *abuf1, uint32_t *lut) {
+                                 uint8_t *abuf1, uint32_t *lut, int tid) {
   constexpr int TM = 16 * MSUB;           // activation rows per workgroup
   constexpr int TN = 16 * NSUB * WV;      // weight rows per workgroup
   constexpr int LPW = 4 * MSUB / WV;      // activation loads per wave per chunk
   static_assert(LPW * WV == 4 * MSUB, "activation loads split evenly");
 
-  const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
   const int r = lane % 16;
@@ -543,7 +543,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu_for(MSUB)))) void gemm_kernel(Ge
   __shared__ __attribute__((aligned(16))) uint8_t abuf1[16 * MSUB * kChunkBytes];
   __shared__ uint32_t lut[256 * LUTC];
   gemm_tile<MSUB, NSUB, LUTC, MODE, WV>(g, static_cast<int>(blockIdx.x),
-                                        static_cast<int>(blockIdx.z), abuf0, abuf1, lut);
+                                        static_cast<int>(blockIdx.z), abuf0, abuf1, lut,
+                                        static_cast<int>(threadIdx.x));
 }
 
 // Dense large-M variant of the same product, software-pipelined by k-step.
@@ -1087,11 +1088,9 @@ hipError_t dispatch(int msub, int nsub, int waves_m, const GemmArgs &g, dim3 gri
 // Items are dealt as gemm_kernel's grid deals its workgroups (moe_item), the
 // grid being a multiple of 8 workgroups, so an item runs on the XCD that
 // workgroup would have.  The 16-token layer's items (about 1100 and 1500)
-// take two rounds each on the 1024 workgroups.  One round would need 6
-// workgroups per compute unit, i.e. at most 80 registers per lane: the
-// compiler then spills, and a reload ahead of the chunk loop makes it wait
-// for every load in flight on each chunk, which costs more than the second
-// round (measured at 16 tokens: 362 against 275 us per call).
+// take two rounds each on the 1024 workgroups; 6 workgroups per compute unit
+// (one round) measured slower: a compute unit's items do not finish sooner
+// when more of them share it.
 //
 // The barrier: after a workgroup barrier one thread of each workgroup
 // releases the workgroup's writes (an agent-scope fence) and counts itself
@@ -1199,13 +1198,14 @@ __global__ __launch_bounds__(kBlockThreads) void moe_block_kernel(BlockArgs b) {
   // the next one's loads refill stages the up epilogue may still be reading
   const int64_t tiles8 = (static_cast<int64_t>(*b.n_tiles) + 7) / 8 * 8;
   for (int64_t it = blk; it < tiles8 * b.up.tiles_n; it += nblk) {
-    gemm_tile<1, 2, 1, kMoEUp, kBlockWaves>(b.up, static_cast<int>(it), 0, abuf0, abuf1, lut);
+    gemm_tile<1, 2, 1, kMoEUp, kBlockWaves>(b.up, static_cast<int>(it), 0, abuf0, abuf1, lut,
+                                            tid);
     __syncthreads();
   }
   grid_barrier(b.bar, 2);
   for (int64_t it = blk; it < tiles8 * b.down.tiles_n; it += nblk) {
     gemm_tile<1, 2, 1, kMoEDown, kBlockWaves>(b.down, static_cast<int>(it), 0, abuf0, abuf1,
-                                              lut);
+                                              lut, tid);
     __syncthreads();
   }
   grid_barrier(b.bar, 3);
