@@ -18,8 +18,9 @@ weight-cache variant (tq4_fp8_cache / tq4_linear_fp8) on the same two shapes.
 
 `roofline` is for the dominant kernel of the headline step: at M=16 the whole
 tq4_linear call is one kernel (rotation fused), so its time per launch is the
-step time.  Steps are captured in a HIP graph and replayed (see time_loop),
-timed with HIP events on the replay stream.  `cpu_baseline` times the fp64
+step time.  Steps are launched back to back behind a spin on the GPU that
+outlasts their submission (see time_loop), timed with HIP events on the
+launch stream.  `cpu_baseline` times the fp64
 CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|none|a,b]
@@ -38,7 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-GRAPH_LEAD_CYCLES = 2_000_000  # GPU spin before a timed replay (~1 ms of shader clock)
+LEAD_MIN_US = 1000.0           # GPU spin ahead of a timed region, at least this long
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
 MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, TFLOP/s
 
@@ -110,41 +111,70 @@ def mall_flush(torch):
     ops.read_probe(_FLUSH["buf"], _FLUSH["sink"])
 
 
+_SPIN = {}
+
+
+def spin_cycles_per_us(torch) -> float:
+    """Cycles of torch.cuda._sleep per microsecond on this GPU (measured once)."""
+    if "rate" not in _SPIN:
+        cycles = 4_000_000
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(10_000)
+        s.record()
+        torch.cuda._sleep(cycles)
+        e.record()
+        torch.cuda.synchronize()
+        _SPIN["rate"] = cycles / (s.elapsed_time(e) * 1e3)
+    return _SPIN["rate"]
+
+
 def time_loop(torch, fn, steps: int, warmup: int) -> float:
     """Average ms per call of fn(i) over exactly `steps` calls.
 
-    The calls are captured once into a HIP graph (the library launches on
-    torch's current stream, which is the capture stream) and the graph is
-    replayed, so the GPU runs them back to back without host launch overhead.
-    `warmup` eager calls and one untimed replay come first, then a device
-    synchronization.  A 512 MiB read then evicts the Infinity Cache, so the
-    timed replay reads every input that the graph's calls do not share from
-    HBM, whatever the step count.  HIP events on the replay stream bracket
-    the timed replay.  The start event and the replay are queued behind the
-    flush and a 1 ms spin on the GPU, which leave the host time to submit
-    the whole graph; so the timed region holds the calls alone, not the
-    host's graph-launch work (measured without them: about 26 us per replay
-    at 20 calls, 1.3 us per call, partly as gaps between the calls).  A
-    device synchronization ends it.
+    `warmup` calls first, then a device synchronization; a few more calls
+    time the host's submission of one call.  A read of a 512 MiB buffer then
+    evicts the Infinity Cache, so the timed calls read every input that they
+    do not share from HBM, whatever the step count.  Behind it the GPU spins
+    (torch.cuda._sleep) for twice the time the host needs to submit all
+    `steps` calls (at least 1 ms); the start event, the calls and the stop
+    event are queued behind the spin on the launch stream (torch's current
+    stream, which the library launches on), so when the spin ends every call
+    is already queued and the GPU runs them back to back: the timed region
+    holds the calls and neither the host's submission nor any launch work
+    of its own.  A device synchronization ends it.  (Captured into a HIP
+    graph and replayed instead, the same calls take the same time each, but
+    each replay adds about 10 us before its first call: measured at M=16,
+    17.0 us per call at 1 call per replay, 7.16 at 20, 6.68 at 100; queued
+    eagerly behind the spin 9.6, 6.84 and 6.61.)  If the host's submission
+    outlasted the spin the result would include its gaps, so that case is
+    reported on stderr.
     """
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(steps):
-            fn(i)
-    graph.replay()
+    n = max(1, min(steps, 8))
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    host_us = (time.perf_counter() - t0) * 1e6 / n
     torch.cuda.synchronize()
+    lead_us = max(LEAD_MIN_US, 2.0 * steps * host_us)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    cycles = int(lead_us * spin_cycles_per_us(torch))
     mall_flush(torch)
-    torch.cuda._sleep(GRAPH_LEAD_CYCLES)
+    torch.cuda._sleep(cycles)
     start.record()
-    graph.replay()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    submit_us = (time.perf_counter() - t0) * 1e6
     stop.record()
     torch.cuda.synchronize()
-    del graph
+    if submit_us > lead_us:
+        print(f"[bench] warning: submitting {steps} calls took {submit_us:.0f} us, longer "
+              f"than the {lead_us:.0f} us spin ahead of them", file=sys.stderr)
     return start.elapsed_time(stop) / steps
 
 
