@@ -136,8 +136,8 @@ def time_loop(torch, fn, steps: int, warmup: int) -> float:
     time the host's submission of one call.  A read of a 512 MiB buffer then
     evicts the Infinity Cache, so the timed calls read every input that they
     do not share from HBM, whatever the step count.  Behind it the GPU spins
-    (torch.cuda._sleep) for twice the time the host needs to submit all
-    `steps` calls (at least 1 ms); the start event, the calls and the stop
+    (torch.cuda._sleep) for four times the time the host needs to submit all
+    `steps` calls plus 0.5 ms (at least 1 ms); the start event, the calls and the stop
     event are queued behind the spin on the launch stream (torch's current
     stream, which the library launches on), so when the spin ends every call
     is already queued and the GPU runs them back to back: the timed region
@@ -159,7 +159,7 @@ def time_loop(torch, fn, steps: int, warmup: int) -> float:
         fn(i)
     host_us = (time.perf_counter() - t0) * 1e6 / n
     torch.cuda.synchronize()
-    lead_us = max(LEAD_MIN_US, 2.0 * steps * host_us)
+    lead_us = max(LEAD_MIN_US, 4.0 * steps * host_us + 500.0)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     cycles = int(lead_us * spin_cycles_per_us(torch))
