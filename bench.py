@@ -178,6 +178,54 @@ def time_loop(torch, fn, steps: int, warmup: int) -> float:
     return start.elapsed_time(stop) / steps
 
 
+def time_graph_replay(torch, fn, steps: int, warmup: int) -> float:
+    """time_loop's calls captured into a HIP graph and replayed instead of
+    queued eagerly (same flush and spin ahead of the timed region); used by
+    --timing-sweep to show what a replay adds per timed region."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    mall_flush(torch)
+    torch.cuda._sleep(int(LEAD_MIN_US * spin_cycles_per_us(torch)))
+    start.record()
+    graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    del graph
+    return start.elapsed_time(stop) / steps
+
+
+def timing_sweep(torch, np, ops, I, dev, sb, copies: int) -> dict:
+    """Per-call time of the headline call against the number of calls in
+    the timed region, eager behind the spin (time_loop) and graph-replayed
+    (time_graph_replay): medians of five regions each."""
+    wl = I.WORKLOADS["dense_m16"]
+    packed = ops.pack(torch.from_numpy(I.weights(wl.n, wl.k, wl.weights)).to(dev), sb)
+    stack = [packed] + [packed.clone() for _ in range(copies - 1)]
+    x = bf16_dev(torch, np, I.activations_bf16(wl.m, wl.k), dev)
+    y = torch.empty((wl.m, wl.n), dtype=torch.float32, device=dev)
+    ws = torch.zeros(ops.linear_workspace_size(wl.m, wl.k, wl.n), dtype=torch.uint8, device=dev)
+
+    def fn(i):
+        ops.linear(x, stack[i % copies], sb, out=y, workspace=ws)
+
+    out = {}
+    for k in (1, 2, 5, 20, 100):
+        e = sorted(time_loop(torch, fn, k, 5) * 1e3 for _ in range(5))
+        g = sorted(time_graph_replay(torch, fn, k, 5) * 1e3 for _ in range(5))
+        out[str(k)] = {"eager_us_per_call": round(e[2], 3), "graph_us_per_call": round(g[2], 3)}
+        log("timing_sweep", f"K={k}: eager {e[2]:.3f} us per call, graph replay {g[2]:.3f}")
+    return out
+
+
 def bf16_dev(torch, np, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
@@ -569,6 +617,9 @@ def main() -> int:
     ap.add_argument("--only", default=None,
                     help="profile helper: run just this workload (no JSON contract)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--timing-sweep", action="store_true",
+                    help="print the headline call's per-call time against the calls per timed "
+                         "region, eager and graph-replayed (no JSON contract)")
     ap.add_argument("--cpu-leg", choices=("single", "all"), default=None,
                     help=argparse.SUPPRESS)
     ap.add_argument("--cpu-workers", type=int, default=1, help=argparse.SUPPRESS)
@@ -599,6 +650,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     sb = I.sign_bits()
 
+    if args.timing_sweep:
+        print(json.dumps({"timing_sweep": timing_sweep(torch, np, ops, I, dev, sb, args.copies)}))
+        return 0
     if args.only:
         if args.only == "rotation_ab":
             r = rotation_ab_leg(torch, np, ops, I, args.steps, args.warmup, args.copies, dev, sb)
